@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decoder-layer ops on one MI355X.
+
+A step is one pass of the four memory-bound ops over one synthetic batch of
+32768 tokens (hidden 2048, 16 q / 8 kv heads of 128, intermediate 6144, bf16):
+rmsnorm -> add_rmsnorm -> mrope (in place) -> swiglu, inputs resident in HBM.
+`value` is the algorithmic bytes of a step over its time (GB/s).  Beside it
+the same run times the decode-step op set (5 tokens x 28 layers of
+add_rmsnorm -> mrope -> swiglu, and the 4-op layer with the post-attention
+norm) replayed from one hipGraph, plus an empty-kernel graph with the same
+node count as the launch floor.
+
+Every duration is taken with HIP events recorded on the stream the kernels
+run on.  The oracle (the fp64 C reference) is timed on a bounded sample of the
+same batch on the host for the CPU baseline.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) per fused op; µs per decode-step op set"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_prefill32k_bf16.json")
+KERNEL_SOURCES = ["norm_rope_swiglu_amd/csrc/swiglu.hip", "norm_rope_swiglu_amd/csrc/device.hpp"]
+
+
+def algorithmic_bytes(op, T, H, I, nq, nkv, D, s):
+    """Bytes an op must move: each input read once, each output written once."""
+    if op == "rmsnorm":
+        return 2 * T * H * s + H * s
+    if op == "add_rmsnorm":
+        return 4 * T * H * s + H * s
+    if op == "mrope":
+        return 2 * (nq + nkv) * D * s * T + 12 * T
+    if op == "swiglu":
+        return 3 * T * I * s
+    raise ValueError(op)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(bytes_per_launch):
+    """HBM bytes per swiglu launch from the committed rocprofv3 --pmc summary,
+    or None when it is missing or the kernel changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_tokens):
+    """The oracle, untouched, on the first n_tokens of the batch (one host thread)."""
+    import numpy as np
+    import oracle
+
+    L = w.layer
+    sl = slice(0, n_tokens)
+    x, res, gamma = L.x[sl].cpu(), L.residual[sl].cpu(), L.gamma.cpu()
+    q, k, gu, pos = L.q[sl].cpu(), L.k[sl].cpu(), L.gate_up[sl].cpu(), w.pos[:, sl].cpu().contiguous()
+    eps = float(np.float32(w.eps))
+    t0 = time.perf_counter()
+    oracle.rmsnorm(x, gamma, eps)
+    oracle.add_rmsnorm(x, res, gamma, eps)
+    oracle.mrope(q, k, pos, w.sections, w.theta)
+    oracle.swiglu(gu)
+    dt = time.perf_counter() - t0
+    byts = sum(algorithmic_bytes(op, n_tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2)
+               for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu"))
+    return {"value": round(byts / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {n_tokens} of {w.tokens} tokens of the step's batch, all four ops, "
+                      "fp64 C oracle on one host thread, same algorithmic-byte count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-replays", type=int, default=500)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the ops are independent per token; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import norm_rope_swiglu_amd as nrs
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    nrs.lib()
+
+    # --- the step's batch, generated on the device
+    T, H, D = 32768, 2048, 128
+    w = W.sweep(seed=0, device=dev, dtype="bf16", hidden=H, head_dim=D, tokens=T)
+    L = w.layer
+    I, nq, nkv = w.inter, w.n_q, w.n_kv
+    s = 2
+    y = torch.empty_like(L.x)
+    y2 = torch.empty_like(L.x)
+    ro = torch.empty_like(L.x)
+    act = torch.empty(T, I, dtype=L.x.dtype, device=dev)
+    q, k = L.q.clone(), L.k.clone()
+    ops = ["rmsnorm", "add_rmsnorm", "mrope", "swiglu"]
+    op_bytes = {op: algorithmic_bytes(op, T, H, I, nq, nkv, D, s) for op in ops}
+    step_bytes = sum(op_bytes.values())
+
+    def run(op):
+        if op == "rmsnorm":
+            nrs.rmsnorm(L.x, L.gamma, w.eps, out=y)
+        elif op == "add_rmsnorm":
+            nrs.add_rmsnorm(L.x, L.residual, L.gamma, w.eps, out=y2, residual_out=ro)
+        elif op == "mrope":
+            nrs.mrope(q, k, w.pos, w.sections, w.theta)
+        else:
+            nrs.swiglu(L.gate_up, out=act)
+
+    # calibration copy of known size (1 GiB), for the counter runs' scale factor
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for op in ops:
+            run(op)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, op in enumerate(ops):
+            run(op)
+            ev[i][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / K
+    per_op = {}
+    for j, op in enumerate(ops):
+        d = sorted(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K))
+        mean_us = 1e3 * sum(d) / K
+        gbs = op_bytes[op] / (mean_us * 1e-6) / 1e9
+        per_op[op] = {"mean_us": round(mean_us, 2), "median_us": round(1e3 * d[K // 2], 2),
+                      "p10_us": round(1e3 * d[K // 10], 2), "p90_us": round(1e3 * d[(9 * K) // 10], 2),
+                      "bytes": op_bytes[op], "GB_s": round(gbs, 1),
+                      "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    print(f"bench: step {step_ms:.3f} ms; " + ", ".join(f"{o} {per_op[o]['mean_us']} us"
+          for o in ops), file=sys.stderr, flush=True)
+
+    # --- decode-step op set, hipGraph replay
+    decode = None
+    if not args.no_decode:
+        dw = W.decode(seed=0, n_layers=28, second_norm=True)
+        pos_d = dw.pos.to(dev)
+        decode = {"workload": "5 sequences x 1 token, hidden 2048, q16/kv8 x 128, intermediate 6144, "
+                              "28 layers, bf16"}
+        for four_op in (False, True):
+            bufs, R = [], dw.layers[0].residual.to(dev)
+            for Ld in dw.layers:
+                d = {"in_x": Ld.x.to(dev), "in_residual": R, "in_gamma": Ld.gamma.to(dev),
+                     "in_y": torch.empty(5, 2048, dtype=torch.bfloat16, device=dev),
+                     "in_residual_out": torch.empty(5, 2048, dtype=torch.bfloat16, device=dev),
+                     "q": Ld.q.to(dev), "k": Ld.k.to(dev), "gate_up": Ld.gate_up.to(dev),
+                     "act_out": torch.empty(5, 6144, dtype=torch.bfloat16, device=dev)}
+                R = d["in_residual_out"]
+                if four_op:
+                    d.update(post_x=Ld.x2.to(dev), post_residual=R, post_gamma=Ld.gamma2.to(dev),
+                             post_y=torch.empty_like(R), post_residual_out=torch.empty_like(R))
+                    R = d["post_residual_out"]
+                bufs.append(d)
+            g = nrs.decode_graph(bufs, pos_d, dw.sections, dw.theta, dw.eps)
+            floor = nrs.null_graph(g.nodes)
+            res = {}
+            for name, gr in (("op_set", g), ("empty_graph_same_nodes", floor)):
+                for _ in range(20):
+                    gr.launch(stream)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.decode_replays):
+                    gr.launch(stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                res[name + "_us_per_step"] = round(1e3 * a.elapsed_time(b) / args.decode_replays, 2)
+            per_layer = (algorithmic_bytes("add_rmsnorm", 5, 2048, 6144, 16, 8, 128, 2) * (2 if four_op else 1)
+                         + algorithmic_bytes("mrope", 5, 2048, 6144, 16, 8, 128, 2)
+                         + algorithmic_bytes("swiglu", 5, 2048, 6144, 16, 8, 128, 2))
+            res.update(nodes=g.nodes, bytes_per_step=28 * per_layer)
+            decode["four_op_layer" if four_op else "three_op_layer"] = res
+            g.close()
+            floor.close()
+        print(f"bench: decode {json.dumps(decode)}", file=sys.stderr, flush=True)
+
+    sw = per_op["swiglu"]
+    achieved = sw["GB_s"]
+    traffic = traffic_from_counters(op_bytes["swiglu"])
+    roofline = {"bound": "hbm", "kernel": "swiglu_kernel<bf16>", "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": op_bytes["swiglu"],
+                "mean_launch_us": sw["mean_us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"bench: cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_tokens)
+
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "config": {"workload": "decoder-layer op set rmsnorm+add_rmsnorm+mrope+swiglu over 32768 "
+                               "tokens, hidden 2048, q16/kv8 x 128, intermediate 6144, bf16",
+                   "tokens": T, "hidden": H, "n_q_heads": nq, "n_kv_heads": nkv, "head_dim": D,
+                   "intermediate": I, "sections": list(w.sections), "theta": w.theta,
+                   "bytes_per_step": step_bytes, "parallelism": "single GPU"},
+        "per_op": per_op, "decode": decode, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,37 @@
+// Kernel launchers of libnrs (internal).  Each enqueues on `stream` and
+// returns hipGetLastError(); arguments are assumed validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nrs {
+
+// Grid cap for the row kernels, which walk their rows in a grid-stride loop:
+// 8 blocks of 256 threads per CU on a 256-CU part.
+constexpr int64_t kMaxResidentBlocks = 2048;
+
+// Largest supported head_dim / 2 (frequency pairs per head).
+constexpr int kMaxHalf = 256;
+
+// Per-pair frequencies theta^(-2j/D), computed on the host in fp64 and passed
+// by value (2 KiB of kernel arguments).
+struct mrope_freqs {
+    double w[kMaxHalf];
+};
+
+hipError_t launch_rmsnorm(void *y, const void *x, const void *gamma, int64_t rows, int64_t hidden,
+                          int64_t x_stride, int64_t y_stride, float eps, int dtype,
+                          hipStream_t stream);
+hipError_t launch_add_rmsnorm(void *y, void *residual_out, const void *x, const void *residual,
+                              const void *gamma, int64_t rows, int64_t hidden, float eps,
+                              int dtype, hipStream_t stream);
+hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
+                        int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t q_stride,
+                        int64_t k_stride, int32_t sec_t, int32_t sec_h, const mrope_freqs &fr,
+                        int dtype, hipStream_t stream);
+hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
+                         int64_t gu_stride, int64_t out_stride, int dtype, hipStream_t stream);
+hipError_t launch_empty(hipStream_t stream);
+
+}  // namespace nrs

@@ -1,0 +1,106 @@
+// SwiGLU over a packed gate_up buffer, gfx950.
+//
+// out = silu(gate) * up with silu(g) = g * sigmoid(g), the "SwiGLU" op of the
+// qwen3-tts-triton post (de.news.hada.io topic 27742, part 3).  Each gate_up
+// row holds [gate | up], `inter` elements each; out rows hold `inter`.
+//
+// Elementwise streaming: a thread handles kUnroll 16-byte chunks per pass,
+// issuing all 2*kUnroll loads (gate and up) before any math, so a 256-thread
+// block keeps 32 KiB of reads in flight.  Chunk -> (row, column) uses a
+// multiply-high division by the fixed chunks-per-row.
+//
+// Numerics: sigmoid(g) = 1/(1 + e^-g) is safe while e^-g stays finite
+// (g >= -80).  Below that, silu(g) * up can still be a normal fp32 number
+// (e.g. g = -95, up = 1e3 gives ~5e-37) while e^g itself is subnormal or 0,
+// so the product is formed on a scaled exponent: g * e^(g + 64) * up, then
+// times e^-64 (twice for g < -150), so precision is lost at most in the last
+// rounding.  Below g = -214 the exact result is under 1e-54 for any finite
+// fp32 up and rounds to a signed zero.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace nrs {
+
+namespace {
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr float kExpM64 = 1.60381089054863785e-28f;  // e^-64
+
+__device__ inline float silu_mul_tail(float g, float u) {
+    if (g >= -150.0f) return ((g * expf(g + 64.0f)) * u) * kExpM64;
+    if (g >= -214.0f) return (((g * expf(g + 128.0f)) * u) * kExpM64) * kExpM64;
+    return __builtin_copysignf(0.0f, -u);
+}
+
+__device__ inline float silu_mul(float g, float u) {
+    if (__builtin_expect(g < -80.0f, 0)) return silu_mul_tail(g, u);
+    const float e = expf(-g);
+    return (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+}
+}  // namespace
+
+template <typename IO>
+__global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gate_up,
+                                                          int32_t total, int32_t cpr,
+                                                          fastdiv div_cpr, int64_t inter,
+                                                          int64_t gu_stride, int64_t out_stride) {
+    using T = io_traits<IO>;
+    constexpr int VEC = T::VEC;
+    const int32_t base = (int32_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 graw[kUnroll], uraw[kUnroll];
+    int64_t orow[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int32_t ci = base + u * kThreads;
+        orow[u] = -1;
+        if (ci < total) {
+            const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
+            const int32_t col = ci - r * cpr;
+            const IO *g = gate_up + (int64_t)r * gu_stride + (int64_t)col * VEC;
+            graw[u] = load16_stream(g);
+            uraw[u] = load16_stream(g + inter);
+            orow[u] = (int64_t)r * out_stride + (int64_t)col * VEC;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (orow[u] < 0) continue;
+        float g[VEC], up[VEC], o[VEC];
+        T::unpack(graw[u], g);
+        T::unpack(uraw[u], up);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = silu_mul(g[e], up[e]);
+        store16_stream(out + orow[u], T::pack(o));
+    }
+}
+
+hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
+                         int64_t gu_stride, int64_t out_stride, int dtype, hipStream_t stream) {
+    const int vec = dtype == 0 ? 4 : 8;
+    const int64_t cpr = inter / vec;
+    const size_t esz = dtype == 0 ? 4 : 2;
+    // launch in row slabs so every chunk index of a launch fits in 31 bits
+    const int64_t max_rows = ((int64_t)1 << 30) / cpr;
+    hipError_t err = hipSuccess;
+    for (int64_t r0 = 0; r0 < rows && err == hipSuccess; r0 += max_rows) {
+        const int64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
+        const int32_t total = (int32_t)(nr * cpr);
+        const int64_t blocks = (total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+        const fastdiv dv = make_fastdiv((uint32_t)cpr);
+        const char *gu = (const char *)gate_up + r0 * gu_stride * esz;
+        char *o = (char *)out + r0 * out_stride * esz;
+        const dim3 grid((unsigned)blocks), block(kThreads);
+        if (dtype == 0)
+            hipLaunchKernelGGL(swiglu_kernel<float>, grid, block, 0, stream, (float *)o,
+                               (const float *)gu, total, (int32_t)cpr, dv, inter, gu_stride,
+                               out_stride);
+        else
+            hipLaunchKernelGGL(swiglu_kernel<__bf16>, grid, block, 0, stream, (__bf16 *)o,
+                               (const __bf16 *)gu, total, (int32_t)cpr, dv, inter, gu_stride,
+                               out_stride);
+        err = hipGetLastError();
+    }
+    return err;
+}
+
+}  // namespace nrs

@@ -1,0 +1,89 @@
+// Argument checks of the C ABI (internal).  Pure C++: no HIP call happens
+// before a check fails, so every error path is testable without a GPU.
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+
+#include "nrs.h"
+
+namespace nrs {
+
+// Widest rows: 512 threads x 16 chunks of 16 bytes (block-per-row kernel).
+constexpr int64_t kMaxHiddenBytes = (int64_t)512 * 16 * 16;
+constexpr int kMaxHeadDim = 512;
+constexpr int64_t kMaxHeads = 1 << 16;
+
+inline int elem_size(int dtype) { return dtype == NRS_F32 ? 4 : 2; }
+inline bool known_dtype(int dtype) { return dtype == NRS_F32 || dtype == NRS_BF16; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool stride_ok(int64_t stride, int dtype) { return (stride * elem_size(dtype)) % 16 == 0; }
+inline int vec_of(int dtype) { return 16 / elem_size(dtype); }
+
+inline int check_rmsnorm(const void *y, const void *x, const void *gamma, int64_t rows,
+                         int64_t hidden, int64_t x_stride, int64_t y_stride, float eps,
+                         int dtype) {
+    if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
+    if (rows < 0 || hidden <= 0 || hidden % vec_of(dtype) != 0 ||
+        hidden * elem_size(dtype) > kMaxHiddenBytes)
+        return NRS_ERR_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return NRS_ERR_ARG;
+    if (rows == 0) return NRS_OK;
+    if (x_stride < hidden || y_stride < hidden) return NRS_ERR_SHAPE;
+    if (!y || !x || !gamma) return NRS_ERR_NULL;
+    if (!aligned16(y) || !aligned16(x) || !aligned16(gamma) || !stride_ok(x_stride, dtype) ||
+        !stride_ok(y_stride, dtype))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
+inline int check_add_rmsnorm(const void *y, const void *residual_out, const void *x,
+                             const void *residual, const void *gamma, int64_t rows,
+                             int64_t hidden, float eps, int dtype) {
+    int st = check_rmsnorm(y, x, gamma, rows, hidden, hidden, hidden, eps, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    if (!residual_out || !residual) return NRS_ERR_NULL;
+    if (!aligned16(residual_out) || !aligned16(residual)) return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
+inline int check_mrope(const void *q, const void *k, const int32_t *pos, int64_t pos_stride,
+                       int64_t tokens, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                       int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_h,
+                       int32_t sec_w, double theta, int dtype) {
+    if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
+    if (tokens < 0 || n_q < 0 || n_kv < 0 || (int64_t)n_q + n_kv > kMaxHeads)
+        return NRS_ERR_SHAPE;
+    if (head_dim <= 0 || head_dim > kMaxHeadDim || head_dim % (2 * vec_of(dtype)) != 0)
+        return NRS_ERR_SHAPE;
+    if (sec_t < 0 || sec_h < 0 || sec_w < 0 || (int64_t)sec_t + sec_h + sec_w != head_dim / 2)
+        return NRS_ERR_SECTIONS;
+    if (!(theta > 0.0) || isinf(theta)) return NRS_ERR_ARG;
+    if (tokens == 0 || n_q + n_kv == 0) return NRS_OK;
+    if (pos_stride < tokens) return NRS_ERR_SHAPE;
+    if ((n_q > 0 && q_stride < (int64_t)n_q * head_dim) ||
+        (n_kv > 0 && k_stride < (int64_t)n_kv * head_dim))
+        return NRS_ERR_SHAPE;
+    if (!pos || (n_q > 0 && !q) || (n_kv > 0 && !k)) return NRS_ERR_NULL;
+    if (((uintptr_t)pos & 3u) != 0) return NRS_ERR_ALIGN;
+    if ((n_q > 0 && (!aligned16(q) || !stride_ok(q_stride, dtype))) ||
+        (n_kv > 0 && (!aligned16(k) || !stride_ok(k_stride, dtype))))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
+inline int check_swiglu(const void *out, const void *gate_up, int64_t rows, int64_t inter,
+                        int64_t gate_up_stride, int64_t out_stride, int dtype) {
+    if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
+    if (rows < 0 || inter <= 0 || inter % vec_of(dtype) != 0 || inter / vec_of(dtype) >= (1 << 30))
+        return NRS_ERR_SHAPE;
+    if (rows == 0) return NRS_OK;
+    if (gate_up_stride < 2 * inter || out_stride < inter) return NRS_ERR_SHAPE;
+    if (!out || !gate_up) return NRS_ERR_NULL;
+    if (!aligned16(out) || !aligned16(gate_up) || !stride_ok(gate_up_stride, dtype) ||
+        !stride_ok(out_stride, dtype))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
+}  // namespace nrs

@@ -1,0 +1,207 @@
+"""Python binding of the C ABI (include/nrs.h): argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every element of
+every result is computed by the HIP kernels in libnrs.so.  Names and
+semantics follow the C entry points:
+
+  rmsnorm      gamma * x / sqrt(mean(x^2) + eps) per row
+  add_rmsnorm  h = round(x + residual) -> residual_out;  y = rmsnorm(h)
+  mrope        in-place multimodal rotary embedding of q and k
+  swiglu       silu(gate) * up over a packed [gate | up] buffer
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._native import BF16, F32, DecodeLayer, DecodeShape, check, lib
+
+_vp = ctypes.c_void_p
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"libnrs takes float32 or bfloat16 tensors, not {t.dtype}")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    d = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("libnrs ops take GPU tensors")
+        if t.device != d:
+            raise ValueError("all tensors of a call must be on one device")
+    return d
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _rows2d(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dim() == 2 and t.stride(1) == 1:
+        return t
+    try:
+        return t.view(-1, t.shape[-1])
+    except RuntimeError as e:
+        raise ValueError(f"{name} must be viewable as [rows, width] with unit inner stride") from e
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    x2 = _rows2d(x, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    y2 = _rows2d(out, "out")
+    d = _dev(x2, gamma, y2)
+    rows, hidden = x2.shape
+    if gamma.shape != (hidden,) or not gamma.is_contiguous() or y2.shape != x2.shape:
+        raise ValueError("gamma must be contiguous [hidden]; out must match x")
+    with torch.cuda.device(d):
+        check(lib().nrs_rmsnorm(y2.data_ptr(), x2.data_ptr(), gamma.data_ptr(), rows, hidden,
+                                x2.stride(0), y2.stride(0), float(eps), _code(x2), _stream(d)),
+              "nrs_rmsnorm")
+    return out
+
+
+def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                out: torch.Tensor | None = None, residual_out: torch.Tensor | None = None):
+    """Returns (y, residual_out).  Passing out=x and/or residual_out=residual
+    updates in place."""
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    ts = (x, residual, out, residual_out)
+    if any(not t.is_contiguous() or t.shape != x.shape for t in ts):
+        raise ValueError("x, residual, out and residual_out must be contiguous and of one shape")
+    d = _dev(*ts, gamma)
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    if gamma.shape != (hidden,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be contiguous [hidden]")
+    with torch.cuda.device(d):
+        check(lib().nrs_add_rmsnorm(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+                                    residual.data_ptr(), gamma.data_ptr(), rows, hidden, float(eps),
+                                    _code(x), _stream(d)), "nrs_add_rmsnorm")
+    return out, residual_out
+
+
+def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: float = 1e6):
+    """In place.  q: [T, n_q, D], k: [T, n_kv, D] with packed heads (token
+    strides free); pos: int32 [3, >=T] with unit inner stride."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [tokens, heads, head_dim]")
+    T, nq, D = q.shape
+    if k.shape[0] != T or k.shape[2] != D:
+        raise ValueError("q and k disagree on tokens or head_dim")
+    for t, n in ((q, "q"), (k, "k")):
+        if t.shape[1] > 0 and (t.stride(2) != 1 or t.stride(1) != D):
+            raise ValueError(f"{n} heads must be packed: strides (token, {D}, 1)")
+    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
+        raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    d = _dev(q, k, pos)
+    st, sh, sw = (int(s) for s in sections)
+    with torch.cuda.device(d):
+        check(lib().nrs_mrope(q.data_ptr(), k.data_ptr(), pos.data_ptr(), pos.stride(0), T, nq,
+                              k.shape[1], D, q.stride(0), k.stride(0), st, sh, sw, float(theta),
+                              _code(q), _stream(d)), "nrs_mrope")
+    return q, k
+
+
+def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    gu = _rows2d(gate_up, "gate_up")
+    rows, two_i = gu.shape
+    if two_i % 2:
+        raise ValueError("gate_up rows must have an even width [gate | up]")
+    inter = two_i // 2
+    if out is None:
+        out = torch.empty(gate_up.shape[:-1] + (inter,), dtype=gate_up.dtype, device=gate_up.device)
+    o2 = _rows2d(out, "out")
+    if o2.shape != (rows, inter):
+        raise ValueError("out must be [rows, inter]")
+    d = _dev(gu, o2)
+    with torch.cuda.device(d):
+        check(lib().nrs_swiglu(o2.data_ptr(), gu.data_ptr(), rows, inter, gu.stride(0),
+                               o2.stride(0), _code(gu), _stream(d)), "nrs_swiglu")
+    return out
+
+
+class Graph:
+    """A recorded hipGraph; holds references to every tensor it binds."""
+
+    def __init__(self, handle: int, keep: list):
+        self._h = handle
+        self._keep = keep
+
+    @property
+    def nodes(self) -> int:
+        n = lib().nrs_graph_node_count(self._h)
+        if n < 0:
+            check(n, "nrs_graph_node_count")
+        return n
+
+    def launch(self, stream: torch.cuda.Stream | None = None) -> None:
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        check(lib().nrs_graph_launch(self._h, s), "nrs_graph_launch")
+
+    def close(self) -> None:
+        if self._h:
+            torch.cuda.synchronize()
+            check(lib().nrs_graph_destroy(self._h), "nrs_graph_destroy")
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_LAYER_KEYS = ("in_y", "in_residual_out", "in_x", "in_residual", "in_gamma", "q", "k", "post_y",
+               "post_residual_out", "post_x", "post_residual", "post_gamma", "act_out", "gate_up")
+
+
+def decode_graph(layers: list[dict], pos: torch.Tensor, sections, theta: float, eps: float) -> Graph:
+    """Record the per-layer op set add_rmsnorm -> mrope -> [add_rmsnorm] ->
+    swiglu of every layer into one graph.  `layers` holds, per layer, tensors
+    under the nrs_decode_layer field names (post_* optional)."""
+    if not layers:
+        raise ValueError("no layers")
+    L0 = layers[0]
+    T, hidden = L0["in_x"].shape
+    nq, D = L0["q"].shape[1], L0["q"].shape[2]
+    nkv = L0["k"].shape[1]
+    inter = L0["act_out"].shape[-1]
+    keep = [pos]
+    arr = (DecodeLayer * len(layers))()
+    for i, L in enumerate(layers):
+        for key in _LAYER_KEYS:
+            t = L.get(key)
+            if t is None:
+                continue
+            if not t.is_contiguous():
+                raise ValueError(f"layer {i} {key} must be contiguous")
+            keep.append(t)
+            setattr(arr[i], key, t.data_ptr())
+    st, sh, sw = (int(s) for s in sections)
+    shape = DecodeShape(T, hidden, inter, nq, nkv, D, pos.data_ptr(), pos.stride(0), st, sh, sw,
+                        float(theta), float(eps), _code(L0["in_x"]))
+    h = _vp()
+    with torch.cuda.device(L0["in_x"].device):
+        check(lib().nrs_decode_graph_create(ctypes.byref(h), ctypes.byref(shape), arr, len(layers)),
+              "nrs_decode_graph_create")
+    return Graph(h.value, keep)
+
+
+def null_graph(n_nodes: int, device=None) -> Graph:
+    """Calibration graph of n_nodes empty kernels."""
+    h = _vp()
+    with torch.cuda.device(device or torch.cuda.current_device()):
+        check(lib().nrs_null_graph_create(ctypes.byref(h), int(n_nodes)), "nrs_null_graph_create")
+    return Graph(h.value, [])

@@ -1,0 +1,183 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/nrs.h
+declares, and rejects every invalid argument on the host before any HIP
+call (no compute call is made here; every call below fails validation)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nrs.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, SECTIONS, ARG, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x10000  # a 16-byte aligned stand-in address; never reaches a kernel here
+U = 0x10008  # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    from norm_rope_swiglu_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        from norm_rope_swiglu_amd import build
+        build.build()
+    return _native.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nrs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("nrs_rmsnorm", "nrs_add_rmsnorm", "nrs_mrope", "nrs_swiglu", "nrs_status_string",
+              "nrs_abi_version", "nrs_decode_graph_create", "nrs_graph_launch"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from norm_rope_swiglu_amd import _native
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(nrs_\w+)", out))
+    declared = set(declared_functions())
+    assert declared <= exported, declared - exported
+    assert exported <= declared, f"exported but undeclared: {exported - declared}"
+    assert declared == set(_native.SIGNATURES), "binding signatures differ from the header"
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.nrs_abi_version() == 1
+    for s in (OK, NULL, SHAPE, ALIGN, DTYPE, SECTIONS, ARG, HIP):
+        assert L.nrs_status_string(s)
+    assert L.nrs_status_string(-99) == b"unknown status"
+    assert L.nrs_last_hip_error() == 0
+
+
+RMS = [  # (y, x, gamma, rows, hidden, x_stride, y_stride, eps, dtype) -> status
+    ((P, P, P, 4, 256, 256, 256, 1e-6, 2), DTYPE),
+    ((P, P, P, -1, 256, 256, 256, 1e-6, 1), SHAPE),
+    ((P, P, P, 4, 0, 256, 256, 1e-6, 1), SHAPE),
+    ((P, P, P, 4, 100, 100, 100, 1e-6, 1), SHAPE),        # not a multiple of 8 bf16
+    ((P, P, P, 4, 258, 258, 258, 1e-6, 0), SHAPE),        # not a multiple of 4 fp32
+    ((P, P, P, 4, 65536 + 8, 65544, 65544, 1e-6, 1), SHAPE),  # wider than supported
+    ((P, P, P, 4, 256, 256, 256, -1e-6, 1), ARG),
+    ((P, P, P, 4, 256, 256, 256, float("nan"), 1), ARG),
+    ((P, P, P, 4, 256, 256, 256, float("inf"), 1), ARG),
+    ((P, P, P, 4, 256, 128, 256, 1e-6, 1), SHAPE),        # stride shorter than a row
+    ((None, P, P, 4, 256, 256, 256, 1e-6, 1), NULL),
+    ((P, None, P, 4, 256, 256, 256, 1e-6, 1), NULL),
+    ((P, P, None, 4, 256, 256, 256, 1e-6, 1), NULL),
+    ((U, P, P, 4, 256, 256, 256, 1e-6, 1), ALIGN),
+    ((P, P, U, 4, 256, 256, 256, 1e-6, 1), ALIGN),
+    ((P, P, P, 4, 256, 258, 256, 1e-6, 0), ALIGN),        # fp32 stride of 1032 bytes
+    ((None, None, None, 0, 256, 256, 256, 1e-6, 1), OK),  # empty: nothing launched
+]
+
+
+@pytest.mark.parametrize("args,want", RMS)
+def test_rmsnorm_rejects(L, args, want):
+    assert L.nrs_rmsnorm(*args, None) == want
+
+
+ADD = [  # (y, residual_out, x, residual, gamma, rows, hidden, eps, dtype)
+    ((P, None, P, P, P, 4, 256, 1e-6, 1), NULL),
+    ((P, P, P, None, P, 4, 256, 1e-6, 1), NULL),
+    ((P, U, P, P, P, 4, 256, 1e-6, 1), ALIGN),
+    ((P, P, P, U, P, 4, 256, 1e-6, 1), ALIGN),
+    ((P, P, P, P, P, 4, 12, 1e-6, 1), SHAPE),
+    ((P, P, P, P, P, 4, 256, -1.0, 0), ARG),
+    ((P, P, P, P, P, 4, 256, 1e-6, -1), DTYPE),
+    ((None, None, None, None, None, 0, 256, 1e-6, 0), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", ADD)
+def test_add_rmsnorm_rejects(L, args, want):
+    assert L.nrs_add_rmsnorm(*args, None) == want
+
+
+def mr(q=P, k=P, pos=P, pos_stride=8, tokens=8, nq=4, nkv=2, D=64, qs=256, ks=128,
+       sec=(8, 12, 12), theta=1e6, dtype=1):
+    return (q, k, pos, pos_stride, tokens, nq, nkv, D, qs, ks, *sec, theta, dtype)
+
+
+MROPE = [
+    (mr(dtype=3), DTYPE),
+    (mr(tokens=-1), SHAPE),
+    (mr(nq=-1), SHAPE),
+    (mr(D=0), SHAPE),
+    (mr(D=72, qs=288, ks=144, sec=(12, 12, 12)), SHAPE),   # bf16 needs D % 16 == 0
+    (mr(D=1024, qs=4096, ks=2048, sec=(128, 192, 192)), SHAPE),
+    (mr(sec=(8, 12, 11)), SECTIONS),
+    (mr(sec=(-1, 21, 12)), SECTIONS),
+    (mr(theta=0.0), ARG),
+    (mr(theta=float("inf")), ARG),
+    (mr(theta=float("nan")), ARG),
+    (mr(pos_stride=7), SHAPE),
+    (mr(qs=200), SHAPE),
+    (mr(ks=64), SHAPE),
+    (mr(pos=None), NULL),
+    (mr(q=None), NULL),
+    (mr(k=None), NULL),
+    (mr(pos=P + 2), ALIGN),
+    (mr(q=U), ALIGN),
+    (mr(qs=260), ALIGN),
+    (mr(q=None, k=None, pos=None, tokens=0), OK),
+    (mr(q=None, k=None, pos=None, nq=0, nkv=0), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", MROPE)
+def test_mrope_rejects(L, args, want):
+    assert L.nrs_mrope(*args, None) == want
+
+
+SWIGLU = [  # (out, gate_up, rows, inter, gate_up_stride, out_stride, dtype)
+    ((P, P, 4, 768, 1536, 768, 9), DTYPE),
+    ((P, P, -2, 768, 1536, 768, 1), SHAPE),
+    ((P, P, 4, 0, 1536, 768, 1), SHAPE),
+    ((P, P, 4, 764, 1528, 764, 1), SHAPE),
+    ((P, P, 4, 768, 1535, 768, 1), SHAPE),
+    ((P, P, 4, 768, 1536, 767, 0), SHAPE),
+    ((None, P, 4, 768, 1536, 768, 1), NULL),
+    ((P, None, 4, 768, 1536, 768, 1), NULL),
+    ((U, P, 4, 768, 1536, 768, 1), ALIGN),
+    ((P, P, 4, 768, 1540, 768, 1), ALIGN),     # 3080-byte bf16 rows
+    ((None, None, 0, 768, 1536, 768, 1), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", SWIGLU)
+def test_swiglu_rejects(L, args, want):
+    assert L.nrs_swiglu(*args, None) == want
+
+
+def test_graph_entry_points_reject(L):
+    from norm_rope_swiglu_amd._native import DecodeLayer, DecodeShape
+    h = ctypes.c_void_p()
+    assert L.nrs_graph_node_count(None) == NULL
+    assert L.nrs_graph_launch(None, None) == NULL
+    assert L.nrs_graph_destroy(None) == OK
+    assert L.nrs_null_graph_create(None, 4) == NULL
+    assert L.nrs_null_graph_create(ctypes.byref(h), 0) == ARG
+    shape = DecodeShape(5, 2048, 6144, 16, 8, 128, P, 5, 16, 24, 24, 1e6, 1e-6, 1)
+    layers = (DecodeLayer * 1)()
+    assert L.nrs_decode_graph_create(None, ctypes.byref(shape), layers, 1) == NULL
+    assert L.nrs_decode_graph_create(ctypes.byref(h), None, layers, 1) == NULL
+    assert L.nrs_decode_graph_create(ctypes.byref(h), ctypes.byref(shape), layers, 0) == ARG
+    # layer pointers left NULL: the first op's check fails before any recording
+    assert L.nrs_decode_graph_create(ctypes.byref(h), ctypes.byref(shape), layers, 1) == NULL
+    bad = DecodeShape(5, 2048, 6144, 16, 8, 128, P, 5, 16, 24, 23, 1e6, 1e-6, 1)
+    for f in DecodeLayer._fields_:
+        setattr(layers[0], f[0], P)
+    layers[0].post_x = None
+    assert L.nrs_decode_graph_create(ctypes.byref(h), ctypes.byref(bad), layers, 1) == SECTIONS
+    assert h.value is None
