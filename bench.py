@@ -117,10 +117,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
     nrs.lib()
 
-    # --- the step's batch, generated on the device
+    # --- the step's batch, generated on the device.  rmsnorm gets its own
+    # input rows so no op reads what the op before it just read.
     T, H, D = 32768, 2048, 128
     w = W.sweep(seed=0, device=dev, dtype="bf16", hidden=H, head_dim=D, tokens=T)
     L = w.layer
+    xn = W.sweep(seed=1, device=dev, dtype="bf16", hidden=H, head_dim=D, tokens=T).layer.x
     I, nq, nkv = w.inter, w.n_q, w.n_kv
     s = 2
     y = torch.empty_like(L.x)
@@ -134,7 +136,7 @@ def main():
 
     def run(op):
         if op == "rmsnorm":
-            nrs.rmsnorm(L.x, L.gamma, w.eps, out=y)
+            nrs.rmsnorm(xn, L.gamma, w.eps, out=y)
         elif op == "add_rmsnorm":
             nrs.add_rmsnorm(L.x, L.residual, L.gamma, w.eps, out=y2, residual_out=ro)
         elif op == "mrope":
@@ -155,27 +157,38 @@ def main():
             run(op)
     torch.cuda.synchronize()
 
+    # the timed steps: K passes of the four ops, back to back, one event pair
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        for j, op in enumerate(ops):
+    for _ in range(K):
+        for op in ops:
             run(op)
-            ev[i][j + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / K
+
+    # per-op launch duration: K launches of one op back to back between two
+    # events (launch latency overlaps the previous launch, as in the step),
+    # repeated R times; mean and spread over the R repeats
     per_op = {}
-    for j, op in enumerate(ops):
-        d = sorted(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K))
-        mean_us = 1e3 * sum(d) / K
+    R = 5
+    for op in ops:
+        reps = []
+        for _ in range(R):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(K):
+                run(op)
+            b.record(stream)
+            torch.cuda.synchronize()
+            reps.append(1e3 * a.elapsed_time(b) / K)
+        reps.sort()
+        mean_us = sum(reps) / R
         gbs = op_bytes[op] / (mean_us * 1e-6) / 1e9
-        per_op[op] = {"mean_us": round(mean_us, 2), "median_us": round(1e3 * d[K // 2], 2),
-                      "p10_us": round(1e3 * d[K // 10], 2), "p90_us": round(1e3 * d[(9 * K) // 10], 2),
-                      "bytes": op_bytes[op], "GB_s": round(gbs, 1),
+        per_op[op] = {"mean_us": round(mean_us, 2), "min_us": round(reps[0], 2),
+                      "max_us": round(reps[-1], 2), "bytes": op_bytes[op], "GB_s": round(gbs, 1),
                       "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     print(f"bench: step {step_ms:.3f} ms; " + ", ".join(f"{o} {per_op[o]['mean_us']} us"
           for o in ops), file=sys.stderr, flush=True)
@@ -225,7 +238,7 @@ def main():
         print(f"bench: decode {json.dumps(decode)}", file=sys.stderr, flush=True)
 
     sw = per_op["swiglu"]
-    achieved = sw["GB_s"]
+    achieved = sw["GB_s"]  # algorithmic bytes per launch / mean launch duration
     traffic = traffic_from_counters(op_bytes["swiglu"])
     roofline = {"bound": "hbm", "kernel": "swiglu_kernel<bf16>", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

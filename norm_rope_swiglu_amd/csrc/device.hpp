@@ -127,4 +127,14 @@ __device__ inline uint32_t div(uint32_t n, const fastdiv &f) {
     return (hi + n) >> f.s;
 }
 
+// Workgroups are dispatched to the 8 XCDs of an MI355X round-robin (block b
+// runs on XCD b % 8).  This remaps block indices so that each XCD walks one
+// contiguous eighth of the index range; blocks past the last multiple of 8
+// keep their index.
+__device__ inline uint32_t xcd_contiguous(uint32_t b, uint32_t nb) {
+    const uint32_t per = nb / 8;
+    if (b >= per * 8) return b;
+    return (b % 8) * per + b / 8;
+}
+
 }  // namespace nrs

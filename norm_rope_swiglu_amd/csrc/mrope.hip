@@ -8,17 +8,17 @@
 // [s_t, s_t + s_h) the height stream and the rest the width stream; pair j
 // turns by p * theta^(-2j/D).
 //
-// Structure: a block owns `tpb` consecutive tokens.
-//   phase 1: for every (token, pair) of the block, the angle p * w_j is formed
-//            in fp64 (w_j computed on the host in fp64), reduced mod 2*pi in
-//            fp64 (Cody-Waite with a two-term 2*pi), and only the reduced
-//            angle, |r| <= pi, goes through fp32 sincosf.  The (cos, sin)
-//            table lives in LDS: one evaluation per token and pair, reused by
-//            all n_q + n_kv heads of the token.
-//   phase 2: every (token, head, chunk) item reads 16 bytes from each half of
-//            the head (elements j..j+VEC-1 and j+D/2..), rotates them with the
-//            table, and writes them back to the same place.  Each item owns
-//            its elements, so the in-place update has no read/write hazard.
+// Structure: a block owns `tpb` consecutive tokens and one thread per
+// (token, head, chunk) item; every item reads 16 bytes from each half of its
+// head (elements j..j+VEC-1 and j+D/2..), rotates them and writes them back
+// to the same place.  Each item owns its elements, so the in-place update has
+// no read/write hazard.  The item's two loads are issued first; while they
+// are in flight the block builds its angle table:
+//   for every (token, pair) of the block the angle p * w_j is formed in fp64
+//   (w_j computed on the host in fp64), reduced mod 2*pi in fp64 (Cody-Waite
+//   with a two-term 2*pi), and only the reduced angle, |r| <= pi, goes through
+//   fp32 sincosf.  The (cos, sin) table lives in LDS: one evaluation per token
+//   and pair, shared by all n_q + n_kv heads of the token.
 // q and k are addressed with their own token strides, so they may sit inside
 // a packed qkv projection output.
 #include "device.hpp"
@@ -30,12 +30,11 @@ namespace {
 constexpr double kTwoPiHi = 6.283185307179586232;      // fp64 nearest to 2*pi
 constexpr double kTwoPiLo = 2.4492935982947064e-16;    // 2*pi - kTwoPiHi
 constexpr double kInvTwoPi = 0.15915494309189533577;
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kMaxThreads = 1024;
 }  // namespace
 
 template <typename IO>
-__global__ __launch_bounds__(kThreads) void mrope_kernel(
+__global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens, int32_t n_q,
     int32_t head_dim, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
     int32_t tpb, int32_t per_tok, int32_t cph, fastdiv div_half, fastdiv div_per_tok,
@@ -45,11 +44,50 @@ __global__ __launch_bounds__(kThreads) void mrope_kernel(
     extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
     const int half = head_dim >> 1;
     const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
     const int64_t tok0 = (int64_t)blockIdx.x * tpb;
     const int ntok = (int)((tokens - tok0) < tpb ? (tokens - tok0) : tpb);
+    const int items = ntok * per_tok;
 
+    // where item i lives, and its slot in the table
+    auto locate = [&](int i, int &tab) -> IO * {
+        const int tl = (int)div((uint32_t)i, div_per_tok);
+        const int rem = i - tl * per_tok;
+        const int head = (int)div((uint32_t)rem, div_cph);
+        const int c = rem - head * cph;
+        const int64_t tok = tok0 + tl;
+        IO *p = head < n_q ? q + tok * q_stride + (int64_t)head * head_dim
+                           : k + tok * k_stride + (int64_t)(head - n_q) * head_dim;
+        tab = tl * half + c * VEC;
+        return p + c * VEC;
+    };
+    auto rotate_store = [&](IO *p, int tab, const u32x4 &lo, const u32x4 &hi) {
+        float a[VEC], b[VEC], ra[VEC], rb[VEC];
+        T::unpack(lo, a);
+        T::unpack(hi, b);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const f32x2 t = table[tab + e];
+            ra[e] = __builtin_fmaf(a[e], t.x, -(b[e] * t.y));
+            rb[e] = __builtin_fmaf(b[e], t.x, a[e] * t.y);
+        }
+        store16_stream(p, T::pack(ra));
+        store16_stream(p + half, T::pack(rb));
+    };
+
+    // 1. this thread's first item: issue its loads before anything else
+    IO *p0 = nullptr;
+    int tab0 = 0;
+    u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
+    if (tid < items) {
+        p0 = locate(tid, tab0);
+        lo0 = load16_stream(p0);
+        hi0 = load16_stream(p0 + half);
+    }
+
+    // 2. the block's angle table
     const int n_ang = ntok * half;
-    for (int e = tid; e < n_ang; e += kThreads) {
+    for (int e = tid; e < n_ang; e += nthreads) {
         const int tl = (int)div((uint32_t)e, div_half);
         const int j = e - tl * half;
         const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
@@ -64,44 +102,14 @@ __global__ __launch_bounds__(kThreads) void mrope_kernel(
     }
     __syncthreads();
 
-    const int items = ntok * per_tok;
-    for (int i0 = tid; i0 < items; i0 += kThreads * kUnroll) {
-        u32x4 lo[kUnroll], hi[kUnroll];
-        IO *ptr[kUnroll];
-        int tab[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int i = i0 + u * kThreads;
-            ptr[u] = nullptr;
-            if (i < items) {
-                const int tl = (int)div((uint32_t)i, div_per_tok);
-                const int rem = i - tl * per_tok;
-                const int head = (int)div((uint32_t)rem, div_cph);
-                const int c = rem - head * cph;
-                const int64_t tok = tok0 + tl;
-                IO *p = head < n_q ? q + tok * q_stride + (int64_t)head * head_dim
-                                   : k + tok * k_stride + (int64_t)(head - n_q) * head_dim;
-                ptr[u] = p + c * VEC;
-                tab[u] = tl * half + c * VEC;
-                lo[u] = load16_stream(ptr[u]);
-                hi[u] = load16_stream(ptr[u] + half);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (ptr[u] == nullptr) continue;
-            float a[VEC], b[VEC], ra[VEC], rb[VEC];
-            T::unpack(lo[u], a);
-            T::unpack(hi[u], b);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const f32x2 t = table[tab[u] + e];
-                ra[e] = __builtin_fmaf(a[e], t.x, -(b[e] * t.y));
-                rb[e] = __builtin_fmaf(b[e], t.x, a[e] * t.y);
-            }
-            store16_stream(ptr[u], T::pack(ra));
-            store16_stream(ptr[u] + half, T::pack(rb));
-        }
+    // 3. rotate; blocks with more items than threads loop over the rest
+    if (p0) rotate_store(p0, tab0, lo0, hi0);
+    for (int i = tid + nthreads; i < items; i += nthreads) {
+        int tab;
+        IO *p = locate(i, tab);
+        const u32x4 lo = load16_stream(p);
+        const u32x4 hi = load16_stream(p + half);
+        rotate_store(p, tab, lo, hi);
     }
 }
 
@@ -113,16 +121,17 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
     const int vec = dtype == 0 ? 4 : 8;
     const int cph = half / vec;
     const int per_tok = (n_q + n_kv) * cph;
-    // ~2048 items per block (8 per thread); the (cos, sin) table stays <= 32 KiB
-    int tpb = (2048 + per_tok - 1) / per_tok;
-    const int lds_cap = 4096 / half;
-    if (tpb > lds_cap) tpb = lds_cap;
+    // about 512 items (threads) per block, whole tokens only; one item per
+    // thread unless a single token has more than kMaxThreads items
+    int tpb = 512 / per_tok;
     if (tpb < 1) tpb = 1;
+    int threads = ((tpb * per_tok + 63) / 64) * 64;
+    if (threads > kMaxThreads) threads = kMaxThreads;
     const int64_t blocks = (tokens + tpb - 1) / tpb;
     const size_t lds = (size_t)tpb * half * sizeof(f32x2);
     const fastdiv dh = make_fastdiv((uint32_t)half), dp = make_fastdiv((uint32_t)per_tok),
                   dc = make_fastdiv((uint32_t)cph);
-    const dim3 grid((unsigned)blocks), block(kThreads);
+    const dim3 grid((unsigned)blocks), block(threads);
     if (dtype == 0)
         hipLaunchKernelGGL(mrope_kernel<float>, grid, block, lds, stream, (float *)q, (float *)k,
                            pos, pos_stride, tokens, n_q, head_dim, q_stride, k_stride, sec_t,

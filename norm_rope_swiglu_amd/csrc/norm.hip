@@ -7,168 +7,126 @@
 // 27742, part 3): h = x + residual is rounded to the storage type, written
 // as residual_out, and normalised in the same pass.
 //
-// Layout: one wave64 owns one row.  Lane l holds chunks l, l+64, l+128, ...
-// of 16 bytes each, so every load instruction of a wave reads 1 KiB of
-// contiguous HBM; the whole row stays in VGPRs between the read, the
-// reduction and the write, so each input byte is read once and each output
-// byte written once.  The sum of squares is reduced with DPP row operations
-// plus four readlanes (no LDS, no barrier).  gamma is read once per wave and
-// kept in registers while the wave walks its rows; the next row's loads are
-// issued before the current row is reduced and written.
+// Layout: a row is split over TPR threads (a power of two, 64..1024), each
+// holding NCH 16-byte chunks (thread t owns chunks t, t+TPR, ...), so every
+// load instruction of a wave reads 1 KiB of contiguous HBM and the row stays
+// in VGPRs between the read, the reduction and the write: each input byte is
+// read once and each output byte written once.  TPR grows with the row so
+// that a thread holds one or two chunks; measured on MI355X, one 16-byte
+// access per thread per stream in a one-shot grid streams faster than
+// threads that walk several chunks or several rows.
 //
-// Rows wider than 16 chunks per lane (more than 8192 bf16 / 4096 fp32
-// elements) go to a block-per-row kernel: each of 512 threads holds up to 16
-// chunks and the per-wave partial sums meet in 32 bytes of LDS.
+// Reduction: DPP row operations plus four readlanes per wave (no LDS, no
+// barrier); rows spanning several waves add their wave sums through a few
+// bytes of LDS and one barrier.  gamma is loaded together with x (it stays
+// in L2 across rows) and applied last.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace nrs {
 
-template <typename IO, int NCH, bool ADD>
-__global__ __launch_bounds__(256) void norm_wave_kernel(
-    IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, int64_t rows,
-    int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
-    using T = io_traits<IO>;
-    constexpr int VEC = T::VEC;
-    const int lane = threadIdx.x & 63;
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (row >= rows) return;
-
-    u32x4 graw[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int idx = lane + 64 * c;
-        graw[c] = idx < nchunks ? load16(gamma + (int64_t)idx * VEC) : u32x4{0, 0, 0, 0};
-    }
-
-    u32x4 xa[NCH], ra[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int idx = lane + 64 * c;
-        xa[c] = u32x4{0, 0, 0, 0};
-        ra[c] = u32x4{0, 0, 0, 0};
-        if (idx < nchunks) {
-            xa[c] = load16_stream(x + row * x_stride + (int64_t)idx * VEC);
-            if (ADD) ra[c] = load16_stream(res + row * x_stride + (int64_t)idx * VEC);
-        }
-    }
-
-    while (true) {
-        const int64_t next = row + nwaves;
-        u32x4 xb[NCH], rb[NCH];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = lane + 64 * c;
-            xb[c] = u32x4{0, 0, 0, 0};
-            rb[c] = u32x4{0, 0, 0, 0};
-            if (next < rows && idx < nchunks) {
-                xb[c] = load16_stream(x + next * x_stride + (int64_t)idx * VEC);
-                if (ADD) rb[c] = load16_stream(res + next * x_stride + (int64_t)idx * VEC);
-            }
-        }
-
-        float v[NCH][VEC];
-        float ss = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            T::unpack(xa[c], v[c]);
-            if (ADD) {
-                float r[VEC];
-                T::unpack(ra[c], r);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) v[c][i] = T::round_trip(v[c][i] + r[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[c][i], v[c][i], ss);
-        }
-        if (ADD) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int idx = lane + 64 * c;
-                if (idx < nchunks)
-                    store16_stream(res_out + row * y_stride + (int64_t)idx * VEC, T::pack(v[c]));
-            }
-        }
-        ss = wave_sum(ss);
-        const float rs = rsqrtf(__builtin_fmaf(ss, inv_h, eps));
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = lane + 64 * c;
-            float g[VEC], o[VEC];
-            T::unpack(graw[c], g);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) o[i] = (v[c][i] * rs) * g[i];
-            if (idx < nchunks) store16_stream(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
-        }
-
-        if (next >= rows) break;
-        row = next;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            xa[c] = xb[c];
-            ra[c] = rb[c];
-        }
-    }
+namespace {
+constexpr int kBlock = 256;  // threads per block when a row uses fewer
 }
 
-constexpr int BLOCK_ROW_THREADS = 512;
-
-template <typename IO, int NCH, bool ADD>
-__global__ __launch_bounds__(BLOCK_ROW_THREADS) void norm_block_kernel(
+template <typename IO, int TPR, int NCH, bool ADD>
+__global__ __launch_bounds__(TPR > kBlock ? TPR : kBlock) void norm_kernel(
     IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, int64_t rows,
     int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    constexpr int NW = BLOCK_ROW_THREADS / 64;
-    __shared__ float partial[NW];
-    const int tid = threadIdx.x;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        float v[NCH][VEC];
-        float ss = 0.0f;
+    constexpr int BLOCK = TPR > kBlock ? TPR : kBlock;
+    constexpr int RPB = BLOCK / TPR;      // rows per block
+    constexpr int WPR = TPR / 64;         // waves per row
+    __shared__ float partial[BLOCK / 64];
+
+    const int t = threadIdx.x % TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const bool live = row < rows;
+
+    u32x4 xr[NCH], rr[NCH], gr[NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + BLOCK_ROW_THREADS * c;
-            u32x4 xr = u32x4{0, 0, 0, 0}, rr = u32x4{0, 0, 0, 0};
-            if (idx < nchunks) {
-                xr = load16_stream(x + row * x_stride + (int64_t)idx * VEC);
-                if (ADD) rr = load16_stream(res + row * x_stride + (int64_t)idx * VEC);
-            }
-            T::unpack(xr, v[c]);
-            if (ADD) {
-                float r[VEC];
-                T::unpack(rr, r);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) v[c][i] = T::round_trip(v[c][i] + r[i]);
-                if (idx < nchunks)
-                    store16_stream(res_out + row * y_stride + (int64_t)idx * VEC, T::pack(v[c]));
-            }
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[c][i], v[c][i], ss);
+    for (int c = 0; c < NCH; ++c) {
+        const int idx = t + TPR * c;
+        xr[c] = rr[c] = gr[c] = u32x4{0, 0, 0, 0};
+        if (live && idx < nchunks) {
+            xr[c] = load16_stream(x + row * x_stride + (int64_t)idx * VEC);
+            if (ADD) rr[c] = load16_stream(res + row * x_stride + (int64_t)idx * VEC);
+            gr[c] = load16(gamma + (int64_t)idx * VEC);
         }
-        ss = wave_sum(ss);
-        if ((tid & 63) == 0) partial[tid >> 6] = ss;
+    }
+
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        float v[VEC];
+        T::unpack(xr[c], v);
+        if (ADD) {
+            float r[VEC];
+            T::unpack(rr[c], r);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) v[i] += r[i];
+            // the stored h: one rounding to the storage type
+            xr[c] = T::pack(v);
+            T::unpack(xr[c], v);
+            const int idx = t + TPR * c;
+            if (live && idx < nchunks)
+                store16_stream(res_out + row * y_stride + (int64_t)idx * VEC, xr[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    }
+    ss = wave_sum(ss);
+    if (WPR > 1) {
+        if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = ss;
         __syncthreads();
-        float tot = 0.0f;
+        const int w0 = (threadIdx.x / TPR) * WPR;
+        ss = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) tot += partial[w];
-        __syncthreads();  // partial[] is rewritten by the next row
-        const float rs = rsqrtf(__builtin_fmaf(tot, inv_h, eps));
+        for (int w = 0; w < WPR; ++w) ss += partial[w0 + w];
+    }
+    if (!live) return;
+    const float rs = rsqrtf(__builtin_fmaf(ss, inv_h, eps));
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + BLOCK_ROW_THREADS * c;
-            if (idx < nchunks) {
-                float g[VEC], o[VEC];
-                T::unpack(load16(gamma + (int64_t)idx * VEC), g);
+    for (int c = 0; c < NCH; ++c) {
+        const int idx = t + TPR * c;
+        if (idx < nchunks) {
+            float v[VEC], g[VEC], o[VEC];
+            T::unpack(xr[c], v);
+            T::unpack(gr[c], g);
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) o[i] = (v[c][i] * rs) * g[i];
-                store16_stream(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
-            }
+            for (int i = 0; i < VEC; ++i) o[i] = (v[i] * rs) * g[i];
+            store16_stream(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
         }
     }
 }
 
 namespace {
+
+// Threads per row: the power of two in [64, 1024] closest to one chunk per
+// thread; rows wider than 1024 chunks give each thread up to 8.
+int threads_per_row(int nchunks) {
+    int tpr = 64;
+    while (tpr < nchunks && tpr < 1024) tpr *= 2;
+    return tpr;
+}
+
+template <typename IO, bool ADD, int TPR>
+void launch_tpr(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, int64_t rows, int32_t nchunks,
+                int64_t xs, int64_t ys, float inv_h, float eps, hipStream_t stream) {
+    constexpr int BLOCK = TPR > kBlock ? TPR : kBlock;
+    constexpr int RPB = BLOCK / TPR;
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(BLOCK);
+    const int nch = (nchunks + TPR - 1) / TPR;
+#define NRS_NORM(N)                                                                            \
+    hipLaunchKernelGGL((norm_kernel<IO, TPR, N, ADD>), grid, block, 0, stream, y, ro, x, r, g, \
+                       rows, nchunks, xs, ys, inv_h, eps)
+    if (nch <= 1) NRS_NORM(1);
+    else if (nch <= 2) NRS_NORM(2);
+    else if (nch <= 4) NRS_NORM(4);
+    else NRS_NORM(8);
+#undef NRS_NORM
+}
 
 template <typename IO, bool ADD>
 hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *res,
@@ -176,39 +134,15 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
                              int64_t y_stride, float eps, hipStream_t stream) {
     constexpr int VEC = io_traits<IO>::VEC;
     const int32_t nchunks = (int32_t)(hidden / VEC);
-    const int per_lane = (nchunks + 63) / 64;
     const float inv_h = (float)(1.0 / (double)hidden);
     IO *Y = (IO *)y, *RO = (IO *)res_out;
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma;
-
-    if (per_lane <= 16) {
-        const int64_t waves_per_block = 4;
-        int64_t blocks = (rows + waves_per_block - 1) / waves_per_block;
-        if (blocks > kMaxResidentBlocks) blocks = kMaxResidentBlocks;
-        const dim3 grid((unsigned)blocks), block(256);
-#define NRS_NORM_WAVE(N)                                                                        \
-    hipLaunchKernelGGL((norm_wave_kernel<IO, N, ADD>), grid, block, 0, stream, Y, RO, X, R, G, \
-                       rows, nchunks, x_stride, y_stride, inv_h, eps)
-        if (per_lane <= 1) NRS_NORM_WAVE(1);
-        else if (per_lane <= 2) NRS_NORM_WAVE(2);
-        else if (per_lane <= 3) NRS_NORM_WAVE(3);
-        else if (per_lane <= 4) NRS_NORM_WAVE(4);
-        else if (per_lane <= 6) NRS_NORM_WAVE(6);
-        else if (per_lane <= 8) NRS_NORM_WAVE(8);
-        else if (per_lane <= 12) NRS_NORM_WAVE(12);
-        else NRS_NORM_WAVE(16);
-#undef NRS_NORM_WAVE
-    } else {
-        const int per_thread = (nchunks + BLOCK_ROW_THREADS - 1) / BLOCK_ROW_THREADS;
-        int64_t blocks = rows < kMaxResidentBlocks ? rows : kMaxResidentBlocks;
-        const dim3 grid((unsigned)blocks), block(BLOCK_ROW_THREADS);
-#define NRS_NORM_BLOCK(N)                                                                        \
-    hipLaunchKernelGGL((norm_block_kernel<IO, N, ADD>), grid, block, 0, stream, Y, RO, X, R, G, \
-                       rows, nchunks, x_stride, y_stride, inv_h, eps)
-        if (per_thread <= 4) NRS_NORM_BLOCK(4);
-        else if (per_thread <= 8) NRS_NORM_BLOCK(8);
-        else NRS_NORM_BLOCK(16);
-#undef NRS_NORM_BLOCK
+    switch (threads_per_row(nchunks)) {
+        case 64: launch_tpr<IO, ADD, 64>(Y, RO, X, R, G, rows, nchunks, x_stride, y_stride, inv_h, eps, stream); break;
+        case 128: launch_tpr<IO, ADD, 128>(Y, RO, X, R, G, rows, nchunks, x_stride, y_stride, inv_h, eps, stream); break;
+        case 256: launch_tpr<IO, ADD, 256>(Y, RO, X, R, G, rows, nchunks, x_stride, y_stride, inv_h, eps, stream); break;
+        case 512: launch_tpr<IO, ADD, 512>(Y, RO, X, R, G, rows, nchunks, x_stride, y_stride, inv_h, eps, stream); break;
+        default: launch_tpr<IO, ADD, 1024>(Y, RO, X, R, G, rows, nchunks, x_stride, y_stride, inv_h, eps, stream); break;
     }
     return hipGetLastError();
 }

@@ -4,9 +4,12 @@
 // qwen3-tts-triton post (de.news.hada.io topic 27742, part 3).  Each gate_up
 // row holds [gate | up], `inter` elements each; out rows hold `inter`.
 //
-// Elementwise streaming: a thread handles kUnroll 16-byte chunks per pass,
-// issuing all 2*kUnroll loads (gate and up) before any math, so a 256-thread
-// block keeps 32 KiB of reads in flight.  Chunk -> (row, column) uses a
+// Elementwise streaming: one thread per 16-byte output chunk, reading the
+// matching gate and up chunks; measured on MI355X, one access per thread per
+// stream in a one-shot grid streams faster than threads that loop over
+// several chunks.  Each XCD takes one contiguous eighth of the chunks
+// (measured ~1.6% faster than the round-robin interleave; the norms and
+// M-RoPE measured faster interleaved).  Chunk -> (row, column) uses a
 // multiply-high division by the fixed chunks-per-row.
 //
 // Numerics: sigmoid(g) = 1/(1 + e^-g) is safe while e^-g stays finite
@@ -23,7 +26,6 @@ namespace nrs {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 constexpr float kExpM64 = 1.60381089054863785e-28f;  // e^-64
 
 __device__ inline float silu_mul_tail(float g, float u) {
@@ -46,32 +48,19 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gat
                                                           int64_t gu_stride, int64_t out_stride) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    const int32_t base = (int32_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-    u32x4 graw[kUnroll], uraw[kUnroll];
-    int64_t orow[kUnroll];
+    const int32_t ci = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * kThreads + threadIdx.x;
+    if (ci >= total) return;
+    const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
+    const int32_t col = ci - r * cpr;
+    const IO *g = gate_up + (int64_t)r * gu_stride + (int64_t)col * VEC;
+    const u32x4 graw = load16_stream(g);
+    const u32x4 uraw = load16_stream(g + inter);
+    float gv[VEC], uv[VEC], o[VEC];
+    T::unpack(graw, gv);
+    T::unpack(uraw, uv);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int32_t ci = base + u * kThreads;
-        orow[u] = -1;
-        if (ci < total) {
-            const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
-            const int32_t col = ci - r * cpr;
-            const IO *g = gate_up + (int64_t)r * gu_stride + (int64_t)col * VEC;
-            graw[u] = load16_stream(g);
-            uraw[u] = load16_stream(g + inter);
-            orow[u] = (int64_t)r * out_stride + (int64_t)col * VEC;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (orow[u] < 0) continue;
-        float g[VEC], up[VEC], o[VEC];
-        T::unpack(graw[u], g);
-        T::unpack(uraw[u], up);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = silu_mul(g[e], up[e]);
-        store16_stream(out + orow[u], T::pack(o));
-    }
+    for (int e = 0; e < VEC; ++e) o[e] = silu_mul(gv[e], uv[e]);
+    store16_stream(out + (int64_t)r * out_stride + (int64_t)col * VEC, T::pack(o));
 }
 
 hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
@@ -85,7 +74,7 @@ hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t i
     for (int64_t r0 = 0; r0 < rows && err == hipSuccess; r0 += max_rows) {
         const int64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
         const int32_t total = (int32_t)(nr * cpr);
-        const int64_t blocks = (total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+        const int64_t blocks = (total + kThreads - 1) / kThreads;
         const fastdiv dv = make_fastdiv((uint32_t)cpr);
         const char *gu = (const char *)gate_up + r0 * gu_stride * esz;
         char *o = (char *)out + r0 * out_stride * esz;
