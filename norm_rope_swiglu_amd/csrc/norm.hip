@@ -50,9 +50,13 @@ __global__ __launch_bounds__(TPR > kBlock ? TPR : kBlock) void norm_kernel(
         const int idx = t + TPR * c;
         xr[c] = rr[c] = gr[c] = u32x4{0, 0, 0, 0};
         if (live && idx < nchunks) {
+            // gamma first: loads return in order, so waiting for x (and the
+            // residual) also covers gamma, and no wait for gamma lands after the
+            // residual_out store (stores count in the same vmcnt on gfx950,
+            // so such a wait would stall on the store's acknowledgement)
+            gr[c] = load16(gamma + (int64_t)idx * VEC);
             xr[c] = load16_stream(x + row * x_stride + (int64_t)idx * VEC);
             if (ADD) rr[c] = load16_stream(res + row * x_stride + (int64_t)idx * VEC);
-            gr[c] = load16(gamma + (int64_t)idx * VEC);
         }
     }
 
