@@ -92,6 +92,60 @@ def cpu_baseline(w, n_tokens):
                       "fp64 C oracle on one host thread, same algorithmic-byte count"}
 
 
+def op_sweep(dev, K=20, R=3):
+    """Per-op launch duration and GB/s on every bandwidth-bound recipe: the
+    2048-token prefill, the packed ragged batch and the 32768-token sweep at
+    every width and dtype (head_dim 128).  Returns a list of records."""
+    import torch
+
+    import norm_rope_swiglu_amd as nrs
+    import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+    cases = [("prefill_bf16", lambda: W.prefill(device=dev)),
+             ("ragged_bf16", lambda: W.ragged(device=dev))]
+    for dt in ("bf16", "f32"):
+        for H in (512, 1024, 1536, 2048, 4096):
+            cases.append((f"sweep_{dt}_h{H}", lambda dt=dt, H=H: W.sweep(device=dev, dtype=dt, hidden=H,
+                                                                          head_dim=128, tokens=32768)))
+    out = []
+    for name, make in cases:
+        w = make()
+        L = w.layer
+        s = 4 if w.dtype == "f32" else 2
+        T, H, I = w.tokens, w.hidden, w.inter
+        y, y2, ro = torch.empty_like(L.x), torch.empty_like(L.x), torch.empty_like(L.x)
+        act = torch.empty(T, I, dtype=L.x.dtype, device=dev)
+        q, k = L.q.clone(), L.k.clone()
+        runs = {"rmsnorm": lambda: nrs.rmsnorm(L.residual, L.gamma, w.eps, out=y),
+                "add_rmsnorm": lambda: nrs.add_rmsnorm(L.x, L.residual, L.gamma, w.eps, out=y2,
+                                                       residual_out=ro),
+                "mrope": lambda: nrs.mrope(q, k, w.pos, w.sections, w.theta),
+                "swiglu": lambda: nrs.swiglu(L.gate_up, out=act)}
+        rec = {"workload": name, "tokens": T, "hidden": H, "dtype": w.dtype}
+        for op, fn in runs.items():
+            for _ in range(3):
+                fn()
+            best = []
+            for _ in range(R):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(K):
+                    fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                best.append(1e3 * a.elapsed_time(b) / K)
+            us = sum(best) / R
+            byts = algorithmic_bytes(op, T, H, I, w.n_q, w.n_kv, w.head_dim, s)
+            rec[op] = {"us": round(us, 2), "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
+                       "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        out.append(rec)
+        print("bench sweep: " + json.dumps(rec), file=sys.stderr, flush=True)
+        del w, L, y, y2, ro, act, q, k
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +155,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--sweep", metavar="FILE",
+                    help="also time every op on every bandwidth-bound recipe, written to FILE as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -249,6 +305,11 @@ def main():
     if not args.no_cpu_baseline:
         print(f"bench: cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_tokens)
+
+    if args.sweep:
+        recs = op_sweep(dev)
+        with open(args.sweep, "w") as f:
+            json.dump(recs, f, indent=1)
 
     value = step_bytes / (step_ms * 1e-3) / 1e9
     out = {
