@@ -80,6 +80,23 @@ __device__ inline void store16_stream(void *p, const u32x4 &v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
+// Access policy of a launch: NT streams data that is touched once (large
+// calls: read and written once, nothing gained by caching it); otherwise the
+// data goes through the caches (small, latency-bound calls whose inputs were
+// just written by the producing op and are still cache-resident).
+template <bool NT> __device__ inline u32x4 load16_policy(const void *p) {
+    if constexpr (NT) return load16_stream(p);
+    else return load16(p);
+}
+
+template <bool NT> __device__ inline void store16_policy(void *p, const u32x4 &v) {
+    if constexpr (NT) store16_stream(p, v);
+    else store16(p, v);
+}
+
+// Calls that move fewer bytes than this run with cached accesses.
+constexpr long long kStreamBytes = 16ll << 20;
+
 // DPP move of a float across lanes of a 16-lane row (bound_ctrl: lanes with
 // no source read 0, which never happens for the patterns used here).
 template <int CTRL> __device__ inline float dpp(float v) {

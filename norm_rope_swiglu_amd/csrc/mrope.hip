@@ -32,7 +32,7 @@ constexpr double kInvTwoPi = 0.15915494309189533577;  // 1 / (2 pi), fp64
 constexpr int kMaxThreads = 1024;
 }  // namespace
 
-template <typename IO>
+template <typename IO, bool NT>
 __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens, int32_t n_q,
     int32_t head_dim, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
@@ -75,8 +75,8 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
             ra[e] = __builtin_fmaf(a[e], t.x, -(b[e] * t.y));
             rb[e] = __builtin_fmaf(b[e], t.x, a[e] * t.y);
         }
-        store16_stream(p, T::pack(ra));
-        store16_stream(p + half, T::pack(rb));
+        store16_policy<NT>(p, T::pack(ra));
+        store16_policy<NT>(p + half, T::pack(rb));
     };
 
     // 1. this thread's first item: issue its loads before anything else
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
     if (tid < items) {
         p0 = locate(tid, tab0);
-        lo0 = load16_stream(p0);
-        hi0 = load16_stream(p0 + half);
+        lo0 = load16_policy<NT>(p0);
+        hi0 = load16_policy<NT>(p0 + half);
     }
 
     // 2. the block's angle table
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     for (int i = tid + nthreads; i < items; i += nthreads) {
         int tab;
         IO *p = locate(i, tab);
-        const u32x4 lo = load16_stream(p);
-        const u32x4 hi = load16_stream(p + half);
+        const u32x4 lo = load16_policy<NT>(p);
+        const u32x4 hi = load16_policy<NT>(p + half);
         rotate_store(p, tab, lo, hi);
     }
 }
@@ -138,14 +138,20 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
                   dq = make_fastdiv((uint32_t)(q_ipt > 0 ? q_ipt : 1)),
                   dk = make_fastdiv((uint32_t)(k_ipt > 0 ? k_ipt : 1)), dc = make_fastdiv((uint32_t)cph);
     const dim3 grid((unsigned)blocks), block(threads);
-    if (dtype == 0)
-        hipLaunchKernelGGL(mrope_kernel<float>, grid, block, lds, stream, (float *)q, (float *)k,
-                           pos, pos_stride, tokens, n_q, head_dim, q_stride, k_stride, sec_t,
-                           sec_t + sec_h, tpb, per_tok, cph, dh, dq, dk, dc, fr);
-    else
-        hipLaunchKernelGGL(mrope_kernel<__bf16>, grid, block, lds, stream, (__bf16 *)q,
-                           (__bf16 *)k, pos, pos_stride, tokens, n_q, head_dim, q_stride,
-                           k_stride, sec_t, sec_t + sec_h, tpb, per_tok, cph, dh, dq, dk, dc, fr);
+    const bool nt = 2 * tokens * (long long)(n_q + n_kv) * head_dim * (dtype == 0 ? 4 : 2) >=
+                    kStreamBytes;
+#define NRS_MROPE(IO, NT)                                                                        \
+    hipLaunchKernelGGL((mrope_kernel<IO, NT>), grid, block, lds, stream, (IO *)q, (IO *)k, pos,  \
+                       pos_stride, tokens, n_q, head_dim, q_stride, k_stride, sec_t,             \
+                       sec_t + sec_h, tpb, per_tok, cph, dh, dq, dk, dc, fr)
+    if (dtype == 0) {
+        if (nt) NRS_MROPE(float, true);
+        else NRS_MROPE(float, false);
+    } else {
+        if (nt) NRS_MROPE(__bf16, true);
+        else NRS_MROPE(__bf16, false);
+    }
+#undef NRS_MROPE
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ namespace nrs {
 // A row is split over WPR waves of 64 threads; each thread holds NCH chunks
 // (thread t of the row owns chunks t, t + 64*WPR, ...).  Rows of one wave are
 // packed four to a block, wider rows get a block each.
-template <typename IO, int WPR, int NCH, bool ADD>
+template <typename IO, int WPR, int NCH, bool ADD, bool NT>
 __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
     IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, int64_t rows,
     int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
@@ -56,8 +56,8 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
             // residual_out store (stores count in the same vmcnt on gfx950,
             // so such a wait would stall on the store's acknowledgement)
             gr[c] = load16(gamma + (int64_t)idx * VEC);
-            xr[c] = load16_stream(x + row * x_stride + (int64_t)idx * VEC);
-            if (ADD) rr[c] = load16_stream(res + row * x_stride + (int64_t)idx * VEC);
+            xr[c] = load16_policy<NT>(x + row * x_stride + (int64_t)idx * VEC);
+            if (ADD) rr[c] = load16_policy<NT>(res + row * x_stride + (int64_t)idx * VEC);
         }
     }
 
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
             T::unpack(xr[c], v);
             const int idx = t + TPR * c;
             if (live && idx < nchunks)
-                store16_stream(res_out + row * y_stride + (int64_t)idx * VEC, xr[c]);
+                store16_policy<NT>(res_out + row * y_stride + (int64_t)idx * VEC, xr[c]);
         }
 #pragma unroll
         for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
             T::unpack(gr[c], g);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) o[i] = (v[i] * rs) * g[i];
-            store16_stream(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
+            store16_policy<NT>(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
         }
     }
 }
@@ -119,14 +119,14 @@ void norm_shape(int nchunks, int &wpr, int &nch) {
     wpr = (nchunks + 64 * nch - 1) / (64 * nch);
 }
 
-template <typename IO, bool ADD, int WPR>
+template <typename IO, bool ADD, int WPR, bool NT>
 void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, int64_t rows,
                   int32_t nchunks, int nch, int64_t xs, int64_t ys, float inv_h, float eps,
                   hipStream_t stream) {
     constexpr int RPB = WPR == 1 ? 4 : 1;
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(64 * WPR * RPB);
 #define NRS_NORM(N)                                                                             \
-    hipLaunchKernelGGL((norm_kernel<IO, WPR, N, ADD>), grid, block, 0, stream, y, ro, x, r, g, \
+    hipLaunchKernelGGL((norm_kernel<IO, WPR, N, ADD, NT>), grid, block, 0, stream, y, ro, x, r, g, \
                        rows, nchunks, xs, ys, inv_h, eps)
     if (nch <= 1) NRS_NORM(1);
     else if (nch <= 2) NRS_NORM(2);
@@ -146,15 +146,21 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
     norm_shape(nchunks, wpr, nch);
     IO *Y = (IO *)y, *RO = (IO *)res_out;
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma;
+    const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
+#define NRS_SHAPE(W)                                                                             \
+    (nt ? launch_shape<IO, ADD, W, true>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride,  \
+                                         inv_h, eps, stream)                                      \
+        : launch_shape<IO, ADD, W, false>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride, \
+                                          inv_h, eps, stream))
     switch (wpr) {
-#define NRS_WPR(W)                                                                                \
-    case W: launch_shape<IO, ADD, W>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride,      \
-                                     inv_h, eps, stream); break
-        NRS_WPR(1); NRS_WPR(2); NRS_WPR(3); NRS_WPR(4); NRS_WPR(8);
-        default: launch_shape<IO, ADD, 16>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride,
-                                           inv_h, eps, stream); break;
-#undef NRS_WPR
+        case 1: NRS_SHAPE(1); break;
+        case 2: NRS_SHAPE(2); break;
+        case 3: NRS_SHAPE(3); break;
+        case 4: NRS_SHAPE(4); break;
+        case 8: NRS_SHAPE(8); break;
+        default: NRS_SHAPE(16); break;
     }
+#undef NRS_SHAPE
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ __device__ inline float silu_mul(float g, float u) {
 }
 }  // namespace
 
-template <typename IO>
+template <typename IO, bool NT>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gate_up,
                                                           int32_t total, int32_t cpr,
                                                           fastdiv div_cpr, int64_t inter,
@@ -53,14 +53,14 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gat
     const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
     const int32_t col = ci - r * cpr;
     const IO *g = gate_up + (int64_t)r * gu_stride + (int64_t)col * VEC;
-    const u32x4 graw = load16_stream(g);
-    const u32x4 uraw = load16_stream(g + inter);
+    const u32x4 graw = load16_policy<NT>(g);
+    const u32x4 uraw = load16_policy<NT>(g + inter);
     float gv[VEC], uv[VEC], o[VEC];
     T::unpack(graw, gv);
     T::unpack(uraw, uv);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[e] = silu_mul(gv[e], uv[e]);
-    store16_stream(out + (int64_t)r * out_stride + (int64_t)col * VEC, T::pack(o));
+    store16_policy<NT>(out + (int64_t)r * out_stride + (int64_t)col * VEC, T::pack(o));
 }
 
 hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
@@ -79,14 +79,18 @@ hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t i
         const char *gu = (const char *)gate_up + r0 * gu_stride * esz;
         char *o = (char *)out + r0 * out_stride * esz;
         const dim3 grid((unsigned)blocks), block(kThreads);
-        if (dtype == 0)
-            hipLaunchKernelGGL(swiglu_kernel<float>, grid, block, 0, stream, (float *)o,
-                               (const float *)gu, total, (int32_t)cpr, dv, inter, gu_stride,
-                               out_stride);
-        else
-            hipLaunchKernelGGL(swiglu_kernel<__bf16>, grid, block, 0, stream, (__bf16 *)o,
-                               (const __bf16 *)gu, total, (int32_t)cpr, dv, inter, gu_stride,
-                               out_stride);
+        const bool nt = 3 * nr * inter * (long long)esz >= kStreamBytes;
+#define NRS_SWIGLU(IO, NT)                                                                        \
+    hipLaunchKernelGGL((swiglu_kernel<IO, NT>), grid, block, 0, stream, (IO *)o, (const IO *)gu, \
+                       total, (int32_t)cpr, dv, inter, gu_stride, out_stride)
+        if (dtype == 0) {
+            if (nt) NRS_SWIGLU(float, true);
+            else NRS_SWIGLU(float, false);
+        } else {
+            if (nt) NRS_SWIGLU(__bf16, true);
+            else NRS_SWIGLU(__bf16, false);
+        }
+#undef NRS_SWIGLU
         err = hipGetLastError();
     }
     return err;

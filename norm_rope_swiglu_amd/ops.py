@@ -38,8 +38,34 @@ def _dev(*ts: torch.Tensor) -> torch.device:
     return d
 
 
+try:
+    _raw_stream = torch._C._cuda_getCurrentRawStream  # the current hipStream_t, no Stream object
+except AttributeError:  # pragma: no cover - older torch
+    _raw_stream = None
+
+
 def _stream(device: torch.device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+class _on:
+    """Make `device` current for the call; free when it already is."""
+
+    __slots__ = ("idx", "prev")
+
+    def __init__(self, device: torch.device):
+        self.idx = device.index
+
+    def __enter__(self):
+        self.prev = torch.cuda.current_device()
+        if self.prev != self.idx:
+            torch.cuda.set_device(self.idx)
+
+    def __exit__(self, *exc):
+        if self.prev != self.idx:
+            torch.cuda.set_device(self.prev)
 
 
 def _rows2d(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -61,7 +87,7 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
     rows, hidden = x2.shape
     if gamma.shape != (hidden,) or not gamma.is_contiguous() or y2.shape != x2.shape:
         raise ValueError("gamma must be contiguous [hidden]; out must match x")
-    with torch.cuda.device(d):
+    with _on(d):
         check(lib().nrs_rmsnorm(y2.data_ptr(), x2.data_ptr(), gamma.data_ptr(), rows, hidden,
                                 x2.stride(0), y2.stride(0), float(eps), _code(x2), _stream(d)),
               "nrs_rmsnorm")
@@ -84,7 +110,7 @@ def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, ep
     rows = x.numel() // hidden if hidden else 0
     if gamma.shape != (hidden,) or not gamma.is_contiguous():
         raise ValueError("gamma must be contiguous [hidden]")
-    with torch.cuda.device(d):
+    with _on(d):
         check(lib().nrs_add_rmsnorm(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
                                     residual.data_ptr(), gamma.data_ptr(), rows, hidden, float(eps),
                                     _code(x), _stream(d)), "nrs_add_rmsnorm")
@@ -106,7 +132,7 @@ def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: 
         raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
     d = _dev(q, k, pos)
     st, sh, sw = (int(s) for s in sections)
-    with torch.cuda.device(d):
+    with _on(d):
         check(lib().nrs_mrope(q.data_ptr(), k.data_ptr(), pos.data_ptr(), pos.stride(0), T, nq,
                               k.shape[1], D, q.stride(0), k.stride(0), st, sh, sw, float(theta),
                               _code(q), _stream(d)), "nrs_mrope")
@@ -125,7 +151,7 @@ def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
     if o2.shape != (rows, inter):
         raise ValueError("out must be [rows, inter]")
     d = _dev(gu, o2)
-    with torch.cuda.device(d):
+    with _on(d):
         check(lib().nrs_swiglu(o2.data_ptr(), gu.data_ptr(), rows, inter, gu.stride(0),
                                o2.stride(0), _code(gu), _stream(d)), "nrs_swiglu")
     return out
