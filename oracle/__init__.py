@@ -37,8 +37,11 @@ def lib():
         L.oracle_mrope.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int,
                                    _i64, _i64, _int, _int, _int, _dbl, _int]
         L.oracle_swiglu.argtypes = [_vp, _vp, _i64, _i64, _i64, _int]
+        L.oracle_mrope_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int,
+                                             _int, _int, _i64, _i64, _i64, _int, _int, _int, _dbl,
+                                             _vp, _vp, _i64, _i64, _int]
         for f in ("oracle_round", "oracle_widen", "oracle_rmsnorm", "oracle_add_rmsnorm",
-                  "oracle_mrope", "oracle_swiglu"):
+                  "oracle_mrope", "oracle_swiglu", "oracle_mrope_kv_append"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -119,6 +122,33 @@ def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: 
     lib().oracle_mrope(_ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(pos), pos.stride(0), T, nq, nkv,
                        D, q.stride(0), k.stride(0), st, sh, sw, float(theta), _code(q))
     return qo, ko
+
+
+def mrope_kv_append(q, k, v, pos, sections, theta, seq_idx, slot, k_cache, v_cache):
+    """q: [T, n_q, D], k and v: [T, n_kv, D] (token strides free); pos int32
+    [3, >=T]; seq_idx, slot int32 [T]; k_cache: float64 [n_seqs, n_kv, max_seq, D]
+    (initial contents, updated copy returned); v_cache: tensor in q's dtype,
+    same shape (updated copy returned).  Returns (q_rot, k_cache, v_cache)."""
+    q, k, v, pos = _cpu(q), _cpu(k), _cpu(v), _cpu(pos)
+    T, nq, D = q.shape
+    nkv = k.shape[1]
+    for t in (q, k, v):
+        assert t.stride(2) == 1 and (t.shape[1] == 0 or t.stride(1) == D) and t.dtype == q.dtype
+    assert v.shape == k.shape and k.shape[0] == T and k.shape[2] == D
+    assert pos.dtype == torch.int32 and pos.stride(1) == 1
+    seq_idx = _cpu(seq_idx).to(torch.int32).contiguous()
+    slot = _cpu(slot).to(torch.int32).contiguous()
+    kc = np.array(k_cache, dtype=np.float64, copy=True, order="C")
+    vc = _cpu(v_cache).clone().contiguous()
+    n_seqs, _, max_seq, _ = kc.shape
+    assert kc.shape == (n_seqs, nkv, max_seq, D) and tuple(vc.shape) == kc.shape and vc.dtype == q.dtype
+    qo = np.empty((T, nq, D), dtype=np.float64)
+    st, sh, sw = (int(x) for x in sections)
+    lib().oracle_mrope_kv_append(_ptr(qo), _ptr(kc), _ptr(vc), _ptr(q), _ptr(k), _ptr(v), _ptr(pos),
+                                 pos.stride(0), T, nq, nkv, D, q.stride(0), k.stride(0), v.stride(0),
+                                 st, sh, sw, float(theta), _ptr(seq_idx), _ptr(slot), n_seqs, max_seq,
+                                 _code(q))
+    return qo, kc, vc
 
 
 def swiglu(gate_up: torch.Tensor) -> np.ndarray:

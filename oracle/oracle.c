@@ -30,6 +30,8 @@
  *     streams; angle = position * frequency in double.
  *   - SwiGLU: gate is the first half of each gate_up row, up the second;
  *     silu(g) = g * sigmoid(g).
+ *   - KV-cache append: one cache [n_kv][max_seq][head_dim] per sequence; each
+ *     token names its sequence and slot; out-of-range tokens write nothing.
  *
  * Parity pins live in the CPU tests (closed forms, invariants, library
  * routines, a hand example); no function here is "parity unpinned".
@@ -38,6 +40,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Stored element -> double.  bf16 is the top half of an fp32 bit pattern. */
@@ -199,6 +202,48 @@ void oracle_mrope(double *q_out, double *k_out, const void *q, const void *k,
         rotate_heads(k_out + t * (int64_t)n_kv_heads * head_dim, k, t * k_token_stride,
                      n_kv_heads, head_dim, c, s, dtype);
     }
+}
+
+/* [P1] "Custom Triton kernels", kernel 3 (KV cache update): each new K, V
+ * head vector is written into its cache at [head][position][:], here with one
+ * cache of [n_kv][max_seq][head_dim] per sequence, so entry (b, h, s) is at
+ * ((b * n_kv + h) * max_seq + s) * head_dim.  Fused with M-RoPE: q is rotated
+ * (returned in q_out), k is rotated and the rotated k goes to the k cache (k
+ * itself is only read), v is copied unchanged into the v cache.  A token whose
+ * sequence index or slot is out of range writes nothing.  k_cache_out holds
+ * double values (the caller fills it beforehand); v_cache holds the storage
+ * type. */
+void oracle_mrope_kv_append(double *q_out, double *k_cache_out, void *v_cache,
+                            const void *q, const void *k, const void *v,
+                            const int32_t *pos, int64_t pos_stride, int64_t tokens, int n_q_heads,
+                            int n_kv_heads, int head_dim, int64_t q_token_stride,
+                            int64_t k_token_stride, int64_t v_token_stride, int sec_t, int sec_h,
+                            int sec_w, double theta, const int32_t *seq_idx, const int32_t *slot,
+                            int64_t n_seqs, int64_t max_seq, int dtype)
+{
+    double *k_rot = (double *)malloc(sizeof(double) * (size_t)(n_kv_heads > 0 ? n_kv_heads : 1) *
+                                     (size_t)head_dim);
+    for (int64_t t = 0; t < tokens; ++t) {
+        /* rotate this token's q and k with the single-token M-RoPE above */
+        const int32_t p3[3] = {pos[t], pos[pos_stride + t], pos[2 * pos_stride + t]};
+        oracle_mrope(q_out + t * (int64_t)n_q_heads * head_dim, k_rot,
+                     (const char *)q + t * q_token_stride * (dtype == ORACLE_F32 ? 4 : 2),
+                     (const char *)k + t * k_token_stride * (dtype == ORACLE_F32 ? 4 : 2), p3, 1, 1,
+                     n_q_heads, n_kv_heads, head_dim, 0, 0, sec_t, sec_h, sec_w, theta, dtype);
+        const int64_t b = seq_idx[t], s = slot[t];
+        if (b < 0 || b >= n_seqs || s < 0 || s >= max_seq) {
+            continue;
+        }
+        for (int h = 0; h < n_kv_heads; ++h) {
+            const int64_t at = ((b * n_kv_heads + h) * max_seq + s) * head_dim;
+            for (int d = 0; d < head_dim; ++d) {
+                k_cache_out[at + d] = k_rot[h * head_dim + d];
+                put(v_cache, at + d, widen(v, t * v_token_stride + (int64_t)h * head_dim + d, dtype),
+                    dtype);
+            }
+        }
+    }
+    free(k_rot);
 }
 
 /* sigmoid, evaluated so that exp never overflows: 1/(1+e^-g) for g >= 0 and

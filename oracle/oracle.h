@@ -34,6 +34,16 @@ void oracle_mrope(double *q_out, double *k_out, const void *q, const void *k,
                   int64_t k_token_stride, int sec_t, int sec_h, int sec_w, double theta,
                   int dtype);
 
+/* q_out[tokens][n_q][D] (double); rotated k into k_cache_out and v into
+ * v_cache, both [n_seqs][n_kv][max_seq][D]; seq_idx/slot[tokens]. */
+void oracle_mrope_kv_append(double *q_out, double *k_cache_out, void *v_cache,
+                            const void *q, const void *k, const void *v,
+                            const int32_t *pos, int64_t pos_stride, int64_t tokens, int n_q_heads,
+                            int n_kv_heads, int head_dim, int64_t q_token_stride,
+                            int64_t k_token_stride, int64_t v_token_stride, int sec_t, int sec_h,
+                            int sec_w, double theta, const int32_t *seq_idx, const int32_t *slot,
+                            int64_t n_seqs, int64_t max_seq, int dtype);
+
 /* out[rows][inter] (double) from gate_up rows [gate | up] of stride gate_up_stride. */
 void oracle_swiglu(double *out, const void *gate_up, int64_t rows, int64_t inter,
                    int64_t gate_up_stride, int dtype);

@@ -37,6 +37,11 @@ MUTANTS = [
     ("sigmoid_sign", "return 1.0 / (1.0 + exp(-g));", "return 1.0 / (1.0 + exp(g));"),
     ("naive_sigmoid_underflow", "double e = exp(g);\n    return e / (1.0 + e);", "return (float)(1.0 / (1.0 + exp(-(double)(float)g)));"),
     ("bf16_truncates", "nearbyint(a / quantum)", "floor(a / quantum)"),
+    ("kv_seq_head_swapped", "const int64_t at = ((b * n_kv_heads + h) * max_seq + s) * head_dim;",
+     "const int64_t at = ((h * n_seqs + b) * max_seq + s) * head_dim;"),
+    ("kv_cache_gets_unrotated_k", "k_cache_out[at + d] = k_rot[h * head_dim + d];",
+     "k_cache_out[at + d] = widen(k, t * k_token_stride + (int64_t)h * head_dim + d, dtype);"),
+    ("kv_slot_ignored", "const int64_t b = seq_idx[t], s = slot[t];", "const int64_t b = seq_idx[t], s = slot[t] > 0 ? 0 : slot[t];"),
     ("bf16_via_fp32", "int e = ilogb(a);", "a = (double)(float)a; int e = ilogb(a);"),
 ]
 

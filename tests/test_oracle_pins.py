@@ -371,3 +371,53 @@ def test_swiglu_large_negative_gate_keeps_tiny_values():
     out = oracle.swiglu(_gu([-95.0, -120.0], [1e3, 1e30]))[0]
     assert out[0] == pytest.approx(-95 * math.exp(-95) * 1e3, rel=1e-14)
     assert out[1] == pytest.approx(-120 * math.exp(-120) * float(np.float32(1e30)), rel=1e-14)
+
+
+# ----------------------------------------------------------------- mrope + KV-cache append
+
+def _kv_case(dt=torch.float32, T=5, nq=2, nkv=2, D=8, n_seqs=3, max_seq=4):
+    q, k = _rand_qk(T, nq, nkv, D, dt)
+    v = torch.from_numpy(rng.standard_normal((T, nkv, D)).astype(np.float32)).to(dt)
+    kc = np.full((n_seqs, nkv, max_seq, D), -7.0)
+    vc = torch.full((n_seqs, nkv, max_seq, D), -3.0).to(dt)
+    return q, k, v, kc, vc
+
+
+def test_kv_append_placement_by_hand():
+    # positions 0: the rotation is the identity, so the cache must hold k and
+    # v themselves at [seq][head][slot][:]
+    q, k, v, kc, vc = _kv_case()
+    seq = torch.tensor([2, 0, 1, 0, 2], dtype=torch.int32)
+    slot = torch.tensor([3, 0, 1, 2, 0], dtype=torch.int32)
+    pos = torch.zeros(3, 5, dtype=torch.int32)
+    qo, kc2, vc2 = oracle.mrope_kv_append(q, k, v, pos, (1, 1, 2), 1e4, seq, slot, kc, vc)
+    for t, (b, s_) in enumerate(zip(seq.tolist(), slot.tolist())):
+        for h in range(2):
+            assert np.array_equal(kc2[b, h, s_], k[t, h].double().numpy())
+            assert torch.equal(vc2[b, h, s_], v[t, h])
+    written = {(b, s_) for b, s_ in zip(seq.tolist(), slot.tolist())}
+    for b in range(3):
+        for s_ in range(4):
+            if (b, s_) not in written:
+                assert np.all(kc2[b, :, s_] == -7.0) and torch.all(vc2[b, :, s_] == -3.0)
+    assert np.array_equal(qo, q.double().numpy())
+
+
+def test_kv_append_rotates_like_mrope_and_skips_out_of_range():
+    for dt in (torch.float32, torch.bfloat16):
+        q, k, v, kc, vc = _kv_case(dt, T=6, nq=3, nkv=2, D=16, n_seqs=2, max_seq=5)
+        seq = torch.tensor([0, 1, 1, 2, 0, -1], dtype=torch.int32)     # 2 and -1: no such sequence
+        slot = torch.tensor([4, 0, 5, 1, -1, 2], dtype=torch.int32)    # 5 and -1: no such slot
+        pos = torch.tensor(rng.integers(0, 3000, (3, 6)), dtype=torch.int32)
+        qo, kc2, vc2 = oracle.mrope_kv_append(q, k, v, pos, (2, 3, 3), 1e6, seq, slot, kc, vc)
+        rq, rk = oracle.mrope(q, k, pos, (2, 3, 3), 1e6)
+        assert np.array_equal(qo, rq)
+        assert np.array_equal(kc2[0, :, 4], rk[0]) and np.array_equal(kc2[1, :, 0], rk[1])
+        assert torch.equal(vc2[0, :, 4], v[0]) and torch.equal(vc2[1, :, 0], v[1])
+        untouched = np.ones((2, 5), bool)
+        untouched[0, 4] = untouched[1, 0] = False
+        for b in range(2):
+            for s_ in range(5):
+                if untouched[b, s_]:
+                    assert np.all(kc2[b, :, s_] == -7.0)
+                    assert torch.all(vc2[b, :, s_] == torch.tensor(-3.0).to(dt))
