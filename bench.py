@@ -44,6 +44,8 @@ def algorithmic_bytes(op, T, H, I, nq, nkv, D, s):
         return 2 * (nq + nkv) * D * s * T + 12 * T
     if op == "swiglu":
         return 3 * T * I * s
+    if op == "mrope_kv_append":   # q in place, k -> k cache, v -> v cache, 3 positions + seq + slot
+        return 2 * (nq + 2 * nkv) * D * s * T + 20 * T
     raise ValueError(op)
 
 
@@ -227,12 +229,12 @@ def main():
 
     # per-op launch duration: K launches of one op back to back between two
     # events (launch latency overlaps the previous launch, as in the step),
-    # repeated R times; mean and spread over the R repeats
+    # repeated NREP times; mean and spread over the repeats
     per_op = {}
-    R = 5
+    NREP = 5
     for op in ops:
         reps = []
-        for _ in range(R):
+        for _ in range(NREP):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(K):
@@ -241,7 +243,7 @@ def main():
             torch.cuda.synchronize()
             reps.append(1e3 * a.elapsed_time(b) / K)
         reps.sort()
-        mean_us = sum(reps) / R
+        mean_us = sum(reps) / NREP
         gbs = op_bytes[op] / (mean_us * 1e-6) / 1e9
         per_op[op] = {"mean_us": round(mean_us, 2), "min_us": round(reps[0], 2),
                       "max_us": round(reps[-1], 2), "bytes": op_bytes[op], "GB_s": round(gbs, 1),
@@ -293,6 +295,35 @@ def main():
             floor.close()
         print(f"bench: decode {json.dumps(decode)}", file=sys.stderr, flush=True)
 
+    # --- ops beyond the four-op step, on the same batch
+    next_ops = {}
+    v = torch.empty_like(L.k).normal_()
+    kc = torch.empty(1, nkv, T, D, dtype=L.k.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    seq0 = torch.zeros(T, dtype=torch.int32, device=dev)
+    slots = torch.arange(T, dtype=torch.int32, device=dev)
+    nxt = {"mrope_kv_append": lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
+                                                          kc, vc, seq0, slots)}
+    for op, fn in nxt.items():
+        for _ in range(3):
+            fn()
+        reps = []
+        for _ in range(NREP):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(K):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            reps.append(1e3 * a.elapsed_time(b) / K)
+        mean_us = sum(reps) / NREP
+        byts = algorithmic_bytes(op, T, H, I, nq, nkv, D, s)
+        next_ops[op] = {"mean_us": round(mean_us, 2), "bytes": byts,
+                        "GB_s": round(byts / (mean_us * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(byts / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del v, kc, vc
+    print(f"bench: next {json.dumps(next_ops)}", file=sys.stderr, flush=True)
+
     sw = per_op["swiglu"]
     achieved = sw["GB_s"]  # algorithmic bytes per launch / mean launch duration
     traffic = traffic_from_counters(op_bytes["swiglu"])
@@ -322,7 +353,8 @@ def main():
                    "tokens": T, "hidden": H, "n_q_heads": nq, "n_kv_heads": nkv, "head_dim": D,
                    "intermediate": I, "sections": list(w.sections), "theta": w.theta,
                    "bytes_per_step": step_bytes, "parallelism": "single GPU"},
-        "per_op": per_op, "decode": decode, "roofline": roofline, "cpu_baseline": cpu,
+        "per_op": per_op, "decode": decode, "next_ops": next_ops, "roofline": roofline,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

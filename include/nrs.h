@@ -73,8 +73,8 @@ int nrs_last_hip_error(void);
  * the mean over the hidden axis of each row ("How to swap": mean over the
  * last dimension, eps inside the root, the weight applied last).
  *   y[rows][y_stride]  out; x[rows][x_stride]  in; gamma[hidden]  in.
- *   hidden: 1..(8192 bf16 | 4096 fp32 per wave path; up to 65536 bf16 / 32768
- *   fp32 in total), a multiple of 8 (bf16) or 4 (fp32); strides >= hidden.
+ *   hidden: a multiple of 8 (bf16) or 4 (fp32), at most 65536 bf16 / 32768
+ *   fp32 elements; strides >= hidden.
  *   eps: >= 0, finite, used as given (fp32).
  *   y == x (exactly) is allowed.
  */
@@ -113,6 +113,32 @@ int nrs_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t 
               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t q_token_stride,
               int64_t k_token_stride, int32_t sec_t, int32_t sec_h, int32_t sec_w, double theta,
               int dtype, void *stream);
+
+/*
+ * M-RoPE fused with the KV-cache append.  [P1] "Custom Triton kernels",
+ * kernel 3 (KV cache update): the new K and V head vectors of a step are
+ * written into the cache at [head][position][:].  Here each of n_seqs
+ * sequences owns a cache [n_kv_heads][max_seq][head_dim]:
+ *   k_cache, v_cache: [n_seqs][n_kv_heads][max_seq][head_dim], 16-byte aligned.
+ *   n_seqs >= 1, 1 <= max_seq <= 2^36.
+ *   seq_idx[tokens], slot[tokens]: int32 device arrays; token t goes to
+ *     sequence seq_idx[t], position slot[t] of that sequence's cache.  A token
+ *     whose index is outside [0, n_seqs) or slot outside [0, max_seq) writes
+ *     no cache entry (the device data is not otherwise checked).
+ *   q: rotated in place exactly as nrs_mrope does.
+ *   k: read only; its rotated values go to k_cache (one trip through memory).
+ *   v[tokens][v_token_stride]: read only; copied unchanged to v_cache.
+ *   pos, sections, theta, head_dim, strides: as for nrs_mrope.
+ * Two tokens naming the same (sequence, slot) race; the caches must not
+ * overlap q, k or v.
+ */
+int nrs_mrope_kv_append(void *q, const void *k, const void *v, const int32_t *pos,
+                        int64_t pos_stride, int64_t tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, int64_t q_token_stride, int64_t k_token_stride,
+                        int64_t v_token_stride, int32_t sec_t, int32_t sec_h, int32_t sec_w,
+                        double theta, void *k_cache, void *v_cache, const int32_t *seq_idx,
+                        const int32_t *slot, int64_t n_seqs, int64_t max_seq, int dtype,
+                        void *stream);
 
 /*
  * SwiGLU, [P2] part 3: out = silu(gate) * up, silu(g) = g * sigmoid(g).

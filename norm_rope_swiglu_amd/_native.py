@@ -50,6 +50,9 @@ SIGNATURES = {
     "nrs_add_rmsnorm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]),
     "nrs_mrope": (_int, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64,
                          _i32, _i32, _i32, _f64, _int, _vp]),
+    "nrs_mrope_kv_append": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64,
+                                   _i64, _i32, _i32, _i32, _f64, _vp, _vp, _vp, _vp, _i64, _i64,
+                                   _int, _vp]),
     "nrs_swiglu": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "nrs_decode_graph_create": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(DecodeShape),
                                        ctypes.POINTER(DecodeLayer), _i32]),

@@ -146,6 +146,26 @@ NRS_API int nrs_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, 
                                         make_freqs(head_dim, theta), dtype, (hipStream_t)stream));
 }
 
+NRS_API int nrs_mrope_kv_append(void *q, const void *k, const void *v, const int32_t *pos,
+                                int64_t pos_stride, int64_t tokens, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int64_t q_token_stride,
+                                int64_t k_token_stride, int64_t v_token_stride, int32_t sec_t,
+                                int32_t sec_h, int32_t sec_w, double theta, void *k_cache,
+                                void *v_cache, const int32_t *seq_idx, const int32_t *slot,
+                                int64_t n_seqs, int64_t max_seq, int dtype, void *stream) {
+    int st = nrs::check_mrope_kv(q, k, v, pos, pos_stride, tokens, n_q_heads, n_kv_heads, head_dim,
+                                 q_token_stride, k_token_stride, v_token_stride, sec_t, sec_h,
+                                 sec_w, theta, k_cache, v_cache, seq_idx, slot, n_seqs, max_seq,
+                                 dtype);
+    if (st != NRS_OK || tokens == 0 || n_q_heads + n_kv_heads == 0) return st;
+    clear_stale_error();
+    return hip_status(nrs::launch_mrope_kv(q, k, v, pos, pos_stride, tokens, n_q_heads, n_kv_heads,
+                                           head_dim, q_token_stride, k_token_stride,
+                                           v_token_stride, sec_t, sec_h,
+                                           make_freqs(head_dim, theta), k_cache, v_cache, seq_idx,
+                                           slot, n_seqs, max_seq, dtype, (hipStream_t)stream));
+}
+
 NRS_API int nrs_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
                        int64_t gate_up_stride, int64_t out_stride, int dtype, void *stream) {
     int st = nrs::check_swiglu(out, gate_up, rows, inter, gate_up_stride, out_stride, dtype);

@@ -30,6 +30,12 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
                         int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t q_stride,
                         int64_t k_stride, int32_t sec_t, int32_t sec_h, const mrope_freqs &fr,
                         int dtype, hipStream_t stream);
+hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t *pos,
+                           int64_t pos_stride, int64_t tokens, int32_t n_q, int32_t n_kv,
+                           int32_t head_dim, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                           int32_t sec_t, int32_t sec_h, const mrope_freqs &fr, void *k_cache,
+                           void *v_cache, const int32_t *seq_idx, const int32_t *slot,
+                           int64_t n_seqs, int64_t max_seq, int dtype, hipStream_t stream);
 hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
                          int64_t gu_stride, int64_t out_stride, int dtype, hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);

@@ -32,14 +32,53 @@ constexpr double kInvTwoPi = 0.15915494309189533577;  // 1 / (2 pi), fp64
 constexpr int kMaxThreads = 1024;
 }  // namespace
 
+// (cos, sin) of every (token, pair) of the block's tokens into LDS: the angle
+// p * w_j in fp64 (w_j from the host in fp64), converted to turns, the nearest
+// whole turn removed in fp64 (exact), and the fraction, |t| <= 1/2, rounded to
+// fp32 for the hardware v_sin_f32 / v_cos_f32, which take turns: measured max
+// abs error 1.3e-7 over [-1/2, 1/2) on MI355X.
+__device__ inline void build_angle_table(f32x2 *table, const int32_t *pos, int64_t pos_stride,
+                                         int64_t tok0, int ntok, int half, int32_t sec_t,
+                                         int32_t sec_th, const fastdiv &div_half,
+                                         const mrope_freqs &fr) {
+    const int n_ang = ntok * half;
+    for (int e = threadIdx.x; e < n_ang; e += blockDim.x) {
+        const int tl = (int)div((uint32_t)e, div_half);
+        const int j = e - tl * half;
+        const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
+        const double p = (double)pos[s * pos_stride + tok0 + tl];
+        const double turns = (p * fr.w[j]) * kInvTwoPi;
+        const float t = (float)(turns - __builtin_rint(turns));
+        table[e] = f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
+    }
+}
+
+// Rotate one item: VEC pairs (a from the first half, b from the second).
+template <typename IO>
+__device__ inline void rotate_chunks(const f32x2 *tab, const u32x4 &lo, const u32x4 &hi,
+                                     u32x4 &rlo, u32x4 &rhi) {
+    using T = io_traits<IO>;
+    constexpr int VEC = T::VEC;
+    float a[VEC], b[VEC], ra[VEC], rb[VEC];
+    T::unpack(lo, a);
+    T::unpack(hi, b);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const f32x2 t = tab[e];
+        ra[e] = __builtin_fmaf(a[e], t.x, -(b[e] * t.y));
+        rb[e] = __builtin_fmaf(b[e], t.x, a[e] * t.y);
+    }
+    rlo = T::pack(ra);
+    rhi = T::pack(rb);
+}
+
 template <typename IO, bool NT>
 __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens, int32_t n_q,
     int32_t head_dim, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
     int32_t tpb, int32_t per_tok, int32_t cph, fastdiv div_half, fastdiv div_q_ipt,
     fastdiv div_k_ipt, fastdiv div_cph, mrope_freqs fr) {
-    using T = io_traits<IO>;
-    constexpr int VEC = T::VEC;
+    constexpr int VEC = io_traits<IO>::VEC;
     extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
     const int half = head_dim >> 1;
     const int tid = threadIdx.x;
@@ -66,17 +105,10 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
         return p + (int64_t)head * head_dim + c * VEC;
     };
     auto rotate_store = [&](IO *p, int tab, const u32x4 &lo, const u32x4 &hi) {
-        float a[VEC], b[VEC], ra[VEC], rb[VEC];
-        T::unpack(lo, a);
-        T::unpack(hi, b);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const f32x2 t = table[tab + e];
-            ra[e] = __builtin_fmaf(a[e], t.x, -(b[e] * t.y));
-            rb[e] = __builtin_fmaf(b[e], t.x, a[e] * t.y);
-        }
-        store16_policy<NT>(p, T::pack(ra));
-        store16_policy<NT>(p + half, T::pack(rb));
+        u32x4 rlo, rhi;
+        rotate_chunks<IO>(table + tab, lo, hi, rlo, rhi);
+        store16_policy<NT>(p, rlo);
+        store16_policy<NT>(p + half, rhi);
     };
 
     // 1. this thread's first item: issue its loads before anything else
@@ -90,19 +122,7 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     }
 
     // 2. the block's angle table
-    const int n_ang = ntok * half;
-    for (int e = tid; e < n_ang; e += nthreads) {
-        const int tl = (int)div((uint32_t)e, div_half);
-        const int j = e - tl * half;
-        const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
-        const double p = (double)pos[s * pos_stride + tok0 + tl];
-        // angle in turns, reduced to [-1/2, 1/2] in fp64 (subtracting the
-        // nearest integer is exact), then the hardware sin/cos, which take
-        // turns: measured max abs error 1.3e-7 over [-1/2, 1/2) on MI355X
-        const double turns = (p * fr.w[j]) * kInvTwoPi;
-        const float t = (float)(turns - __builtin_rint(turns));
-        table[e] = f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
-    }
+    build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half, fr);
     __syncthreads();
 
     // 3. rotate; blocks with more items than threads loop over the rest
@@ -114,6 +134,139 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
         const u32x4 hi = load16_policy<NT>(p + half);
         rotate_store(p, tab, lo, hi);
     }
+}
+
+// M-RoPE fused with the KV-cache append ("Optimising autoregressive speech
+// models", "Custom Triton kernels", kernel 3: each new K, V head vector goes
+// to its cache at [head][position][:]).  Here every sequence owns a cache
+// [n_kv][max_seq][head_dim] and each token names its sequence and slot.  q is
+// rotated in place; k is rotated straight into the k cache (k itself is only
+// read, so the rotated k makes a single trip to memory); v is copied into the
+// v cache.  Items are ordered q, then k, then v per block, two 16-byte chunks
+// (a pair-half each) per item, all loads issued before the angle table is
+// built.  A token whose sequence index or slot is out of range writes no
+// cache entry.
+template <typename IO, bool NT>
+__global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
+    IO *q, const IO *k, const IO *v, const int32_t *pos, int64_t pos_stride, int64_t tokens,
+    int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t q_stride, int64_t k_stride,
+    int64_t v_stride, int32_t sec_t, int32_t sec_th, int32_t tpb, int32_t cph, fastdiv div_half,
+    fastdiv div_q_ipt, fastdiv div_kv_ipt, fastdiv div_cph, IO *k_cache, IO *v_cache,
+    const int32_t *seq_idx, const int32_t *slot, int64_t n_seqs, int64_t max_seq,
+    mrope_freqs fr) {
+    constexpr int VEC = io_traits<IO>::VEC;
+    extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
+    const int half = head_dim >> 1;
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int64_t tok0 = (int64_t)blockIdx.x * tpb;
+    const int ntok = (int)((tokens - tok0) < tpb ? (tokens - tok0) : tpb);
+    const int q_items = ntok * n_q * cph;
+    const int kv_items = ntok * n_kv * cph;
+    const int items = q_items + 2 * kv_items;
+
+    // item i -> source pointer, destination pointer (nullptr: skip), table
+    // slot, and whether it is rotated (q, k) or copied (v)
+    auto locate = [&](int i, IO *&dst, int &tab, bool &rotate) -> const IO * {
+        const int kind = i < q_items ? 0 : (i < q_items + kv_items ? 1 : 2);
+        const int j = kind == 0 ? i : (kind == 1 ? i - q_items : i - q_items - kv_items);
+        const int hpt = kind == 0 ? n_q : n_kv;
+        const int tl = (int)div((uint32_t)j, kind == 0 ? div_q_ipt : div_kv_ipt);
+        const int rem = j - tl * hpt * cph;
+        const int head = (int)div((uint32_t)rem, div_cph);
+        const int c = rem - head * cph;
+        const int64_t tok = tok0 + tl;
+        tab = tl * half + c * VEC;
+        rotate = kind != 2;
+        const int64_t off = (int64_t)head * head_dim + c * VEC;
+        if (kind == 0) {
+            dst = q + tok * q_stride + off;
+            return dst;
+        }
+        const int64_t b = seq_idx[tok], s = slot[tok];
+        dst = (b >= 0 && b < n_seqs && s >= 0 && s < max_seq)
+                  ? (kind == 1 ? k_cache : v_cache) + ((b * n_kv + head) * max_seq + s) * head_dim +
+                        c * VEC
+                  : nullptr;
+        return (kind == 1 ? k + tok * k_stride : v + tok * v_stride) + off;
+    };
+    auto finish = [&](IO *dst, int tab, bool rotate, const u32x4 &lo, const u32x4 &hi) {
+        u32x4 olo = lo, ohi = hi;
+        if (rotate) rotate_chunks<IO>(table + tab, lo, hi, olo, ohi);
+        store16_policy<NT>(dst, olo);
+        store16_policy<NT>(dst + half, ohi);
+    };
+
+    // 1. this thread's first item: issue its loads before anything else
+    IO *d0 = nullptr;
+    int tab0 = 0;
+    bool rot0 = false;
+    u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
+    if (tid < items) {
+        const IO *src = locate(tid, d0, tab0, rot0);
+        if (d0) {
+            lo0 = load16_policy<NT>(src);
+            hi0 = load16_policy<NT>(src + half);
+        }
+    }
+
+    // 2. the block's angle table
+    build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half, fr);
+    __syncthreads();
+
+    // 3. rotate or copy; blocks with more items than threads loop over the rest
+    if (d0) finish(d0, tab0, rot0, lo0, hi0);
+    for (int i = tid + nthreads; i < items; i += nthreads) {
+        IO *dst;
+        int tab;
+        bool rot;
+        const IO *src = locate(i, dst, tab, rot);
+        if (!dst) continue;
+        const u32x4 lo = load16_policy<NT>(src);
+        const u32x4 hi = load16_policy<NT>(src + half);
+        finish(dst, tab, rot, lo, hi);
+    }
+}
+
+hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t *pos,
+                           int64_t pos_stride, int64_t tokens, int32_t n_q, int32_t n_kv,
+                           int32_t head_dim, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                           int32_t sec_t, int32_t sec_h, const mrope_freqs &fr, void *k_cache,
+                           void *v_cache, const int32_t *seq_idx, const int32_t *slot,
+                           int64_t n_seqs, int64_t max_seq, int dtype, hipStream_t stream) {
+    const int half = head_dim / 2;
+    const int vec = dtype == 0 ? 4 : 8;
+    const int cph = half / vec;
+    const int per_tok = (n_q + 2 * n_kv) * cph;
+    int tpb = 512 / per_tok;
+    if (tpb < 1) tpb = 1;
+    int threads = ((tpb * per_tok + 63) / 64) * 64;
+    if (threads > kMaxThreads) threads = kMaxThreads;
+    const int64_t blocks = (tokens + tpb - 1) / tpb;
+    const size_t lds = (size_t)tpb * half * sizeof(f32x2);
+    const int q_ipt = n_q * cph, kv_ipt = n_kv * cph;
+    const fastdiv dh = make_fastdiv((uint32_t)half),
+                  dq = make_fastdiv((uint32_t)(q_ipt > 0 ? q_ipt : 1)),
+                  dkv = make_fastdiv((uint32_t)(kv_ipt > 0 ? kv_ipt : 1)),
+                  dc = make_fastdiv((uint32_t)cph);
+    const dim3 grid((unsigned)blocks), block(threads);
+    const bool nt = tokens * (long long)(2 * n_q + 4 * n_kv) * head_dim * (dtype == 0 ? 4 : 2) >=
+                    kStreamBytes;
+#define NRS_MROPE_KV(IO, NT)                                                                    \
+    hipLaunchKernelGGL((mrope_kv_kernel<IO, NT>), grid, block, lds, stream, (IO *)q,            \
+                       (const IO *)k, (const IO *)v, pos, pos_stride, tokens, n_q, n_kv,         \
+                       head_dim, q_stride, k_stride, v_stride, sec_t, sec_t + sec_h, tpb, cph,   \
+                       dh, dq, dkv, dc, (IO *)k_cache, (IO *)v_cache, seq_idx, slot, n_seqs,     \
+                       max_seq, fr)
+    if (dtype == 0) {
+        if (nt) NRS_MROPE_KV(float, true);
+        else NRS_MROPE_KV(float, false);
+    } else {
+        if (nt) NRS_MROPE_KV(__bf16, true);
+        else NRS_MROPE_KV(__bf16, false);
+    }
+#undef NRS_MROPE_KV
+    return hipGetLastError();
 }
 
 hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,

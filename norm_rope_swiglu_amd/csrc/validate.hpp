@@ -72,6 +72,28 @@ inline int check_mrope(const void *q, const void *k, const int32_t *pos, int64_t
     return NRS_OK;
 }
 
+inline int check_mrope_kv(const void *q, const void *k, const void *v, const int32_t *pos,
+                          int64_t pos_stride, int64_t tokens, int32_t n_q, int32_t n_kv,
+                          int32_t head_dim, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                          int32_t sec_t, int32_t sec_h, int32_t sec_w, double theta,
+                          const void *k_cache, const void *v_cache, const int32_t *seq_idx,
+                          const int32_t *slot, int64_t n_seqs, int64_t max_seq, int dtype) {
+    int st = check_mrope(q, k, pos, pos_stride, tokens, n_q, n_kv, head_dim, q_stride, k_stride,
+                         sec_t, sec_h, sec_w, theta, dtype);
+    if (st != NRS_OK) return st;
+    if (n_seqs <= 0 || max_seq <= 0 || max_seq > ((int64_t)1 << 36)) return NRS_ERR_SHAPE;
+    // cache elements n_seqs * n_kv * max_seq * head_dim must fit in 62 bits
+    if (n_kv > 0 && n_seqs > ((int64_t)1 << 62) / ((int64_t)n_kv * max_seq * head_dim))
+        return NRS_ERR_SHAPE;
+    if (tokens == 0 || n_q + n_kv == 0) return NRS_OK;
+    if (n_kv > 0 && v_stride < (int64_t)n_kv * head_dim) return NRS_ERR_SHAPE;
+    if (n_kv > 0 && (!v || !k_cache || !v_cache || !seq_idx || !slot)) return NRS_ERR_NULL;
+    if (n_kv > 0 && (!aligned16(v) || !stride_ok(v_stride, dtype) || !aligned16(k_cache) ||
+                     !aligned16(v_cache) || ((uintptr_t)seq_idx & 3u) || ((uintptr_t)slot & 3u)))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
 inline int check_swiglu(const void *out, const void *gate_up, int64_t rows, int64_t inter,
                         int64_t gate_up_stride, int64_t out_stride, int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;

@@ -139,6 +139,37 @@ def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: 
     return q, k
 
 
+def mrope_kv_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, sections,
+                    theta: float, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    seq_idx: torch.Tensor, slot: torch.Tensor):
+    """q rotated in place; rotated k and v written to k_cache / v_cache
+    [n_seqs, n_kv, max_seq, D] at (seq_idx[t], slot[t]).  Returns q."""
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q: [T, n_q, D]; k, v: [T, n_kv, D]")
+    T, nq, D = q.shape
+    nkv = k.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.shape[1] > 0 and (t.stride(2) != 1 or t.stride(1) != D):
+            raise ValueError(f"{n} heads must be packed: strides (token, {D}, 1)")
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4 or k_cache.shape[1] != nkv or \
+            k_cache.shape[3] != D or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("k_cache, v_cache must be contiguous [n_seqs, n_kv, max_seq, D]")
+    for t, n in ((seq_idx, "seq_idx"), (slot, "slot")):
+        if t.dtype != torch.int32 or t.shape != (T,) or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous int32 [tokens]")
+    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
+        raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    d = _dev(q, k, v, pos, k_cache, v_cache, seq_idx, slot)
+    st, sh, sw = (int(s) for s in sections)
+    with _on(d):
+        check(lib().nrs_mrope_kv_append(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), pos.data_ptr(), pos.stride(0), T, nq, nkv, D,
+            q.stride(0), k.stride(0), v.stride(0), st, sh, sw, float(theta), k_cache.data_ptr(),
+            v_cache.data_ptr(), seq_idx.data_ptr(), slot.data_ptr(), k_cache.shape[0],
+            k_cache.shape[2], _code(q), _stream(d)), "nrs_mrope_kv_append")
+    return q
+
+
 def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     gu = _rows2d(gate_up, "gate_up")
     rows, two_i = gu.shape

@@ -140,6 +140,38 @@ def test_mrope_rejects(L, args, want):
     assert L.nrs_mrope(*args, None) == want
 
 
+def kv(q=P, k=P, v=P, pos=P, pos_stride=8, tokens=8, nq=4, nkv=2, D=64, qs=256, ks=128, vs=128,
+       sec=(8, 12, 12), theta=1e6, kc=P, vc=P, seq=P, slot=P, n_seqs=2, max_seq=16, dtype=1):
+    return (q, k, v, pos, pos_stride, tokens, nq, nkv, D, qs, ks, vs, *sec, theta, kc, vc, seq, slot,
+            n_seqs, max_seq, dtype)
+
+
+KV = [
+    (kv(dtype=5), DTYPE),
+    (kv(sec=(8, 12, 13)), SECTIONS),
+    (kv(n_seqs=0), SHAPE),
+    (kv(max_seq=0), SHAPE),
+    (kv(max_seq=(1 << 36) + 1), SHAPE),
+    (kv(vs=64), SHAPE),
+    (kv(v=None), NULL),
+    (kv(kc=None), NULL),
+    (kv(vc=None), NULL),
+    (kv(seq=None), NULL),
+    (kv(slot=None), NULL),
+    (kv(v=U), ALIGN),
+    (kv(kc=U), ALIGN),
+    (kv(vs=132), ALIGN),
+    (kv(seq=P + 1), ALIGN),
+    (kv(slot=P + 2), ALIGN),
+    (kv(q=None, k=None, v=None, pos=None, kc=None, vc=None, seq=None, slot=None, tokens=0), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", KV)
+def test_mrope_kv_append_rejects(L, args, want):
+    assert L.nrs_mrope_kv_append(*args, None) == want
+
+
 SWIGLU = [  # (out, gate_up, rows, inter, gate_up_stride, out_stride, dtype)
     ((P, P, 4, 768, 1536, 768, 9), DTYPE),
     ((P, P, -2, 768, 1536, 768, 1), SHAPE),

@@ -1,0 +1,125 @@
+"""GPU parity of the ops beyond the four-op hot path, through the C ABI,
+against the fp64 oracle: M-RoPE fused with the KV-cache append."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import norm_rope_swiglu_amd as nrs
+import oracle
+import workloads as W
+from parity import check, check_exact
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -7.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    nrs.lib()
+
+
+def _v_for(w, seed=5):
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(w.layer.k.shape, generator=g, dtype=torch.float64).to(torch.float32)
+    return v.to(w.layer.k.dtype).to(w.layer.k.device)
+
+
+def kv_parity(w, seq_idx, slot, n_seqs, max_seq, tag, rows=None):
+    """Run nrs.mrope_kv_append on the workload's q/k (v drawn here) and check
+    q, every written cache entry, and that every other entry is untouched."""
+    L = w.layer
+    dev = "cuda"
+    dt = L.q.dtype
+    q, k = L.q.to(dev).clone(), L.k.to(dev)
+    v = _v_for(w).to(dev)
+    pos = w.pos.to(dev)
+    seq_idx = torch.as_tensor(seq_idx, dtype=torch.int32).to(dev)
+    slot = torch.as_tensor(slot, dtype=torch.int32).to(dev)
+    T, nkv, D = k.shape
+    kc = torch.full((n_seqs, nkv, max_seq, D), SENTINEL, dtype=dt, device=dev)
+    vc = torch.full_like(kc, SENTINEL)
+    q0 = q.clone()
+    nrs.mrope_kv_append(q, k, v, pos, w.sections, w.theta, kc, vc, seq_idx, slot)
+    torch.cuda.synchronize()
+
+    valid = (seq_idx >= 0) & (seq_idx < n_seqs) & (slot >= 0) & (slot < max_seq)
+    # untouched entries keep the sentinel bit for bit
+    written = torch.zeros(n_seqs, max_seq, dtype=torch.bool, device=dev)
+    written[seq_idx[valid].long(), slot[valid].long()] = True
+    keep = ~written[:, None, :, None].expand_as(kc)
+    assert torch.all(kc[keep] == SENTINEL) and torch.all(vc[keep] == SENTINEL), f"{tag}: stray writes"
+
+    sel = torch.arange(T, device=dev) if rows is None else rows.to(dev)
+    sel = sel[valid[sel]]
+    # the oracle with each selected token in its own one-slot cache
+    n = int(sel.numel())
+    qs_, ks_, vs_ = q0[sel].cpu(), k[sel].cpu(), v[sel].cpu()
+    ps_ = pos[:, sel].cpu().contiguous()
+    ident = torch.arange(n, dtype=torch.int32)
+    rq, rkc, rvc = oracle.mrope_kv_append(qs_, ks_, vs_, ps_, w.sections, w.theta, ident,
+                                          torch.zeros(n, dtype=torch.int32),
+                                          np.zeros((n, nkv, 1, D)), torch.zeros(n, nkv, 1, D, dtype=dt))
+    b, s = seq_idx[sel].long(), slot[sel].long()
+    check(f"{tag}/q", q[sel], rq, pairs=True)
+    check(f"{tag}/k_cache", kc[b, :, s, :], rkc[:, :, 0, :], pairs=True)
+    check_exact(f"{tag}/v_cache", vc[b, :, s, :], rvc[:, :, 0, :])
+
+
+def test_kv_append_decode_step():
+    w = W.decode(n_layers=1)
+    p = w.pos[0]
+    kv_parity(w, seq_idx=list(range(5)), slot=p, n_seqs=5, max_seq=2048, tag="kv/decode")
+
+
+def test_kv_append_prefill():
+    w = W.prefill()
+    kv_parity(w, seq_idx=[0] * w.tokens, slot=list(range(w.tokens)), n_seqs=1, max_seq=4096,
+              tag="kv/prefill")
+
+
+def test_kv_append_ragged():
+    w = W.ragged(device="cuda")
+    seq, slot = [], []
+    for i, L in enumerate(w.seq_lens):
+        seq += [i] * L
+    slot = w.pos[0].cpu().tolist()            # each sequence's own positions (offset + index)
+    kv_parity(w, seq_idx=seq, slot=slot, n_seqs=len(w.seq_lens), max_seq=2560, tag="kv/ragged")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kv_append_skips_out_of_range(dtype):
+    w = W.sweep(dtype=dtype, hidden=512, head_dim=64, tokens=40)
+    seq = [t % 3 for t in range(40)]
+    slot = [t for t in range(40)]
+    seq[3], seq[7], slot[11], slot[13] = -1, 3, -2, 40     # nonexistent sequence / slot
+    kv_parity(w, seq_idx=seq, slot=slot, n_seqs=3, max_seq=40, tag=f"kv/skip/{dtype}")
+
+
+@pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 1), (128, (16, 24, 24), 16, 8),
+                                          (256, (32, 48, 48), 4, 2)])
+def test_kv_append_head_shapes(D, sec, nq, nkv):
+    for dt in (torch.float32, torch.bfloat16):
+        g = torch.Generator().manual_seed(D)
+        T = 37
+        w = W.Workload("kvshape", "f32" if dt == torch.float32 else "bf16", T, nq * D, 0, nq, nkv, D,
+                       sec, 1e4, 1e-6, torch.randint(0, 9000, (3, T), generator=g, dtype=torch.int32))
+        q = torch.randn(T, nq, D, generator=g).to(dt)
+        k = torch.randn(T, nkv, D, generator=g).to(dt)
+        w.layers.append(W.Layer(None, None, None, q, k, None))
+        perm = torch.randperm(T, generator=g)
+        kv_parity(w, seq_idx=(perm % 2).tolist(), slot=(perm // 2).tolist(), n_seqs=2, max_seq=19,
+                  tag=f"kv/shape{D}/{dt}")
+
+
+def test_kv_append_full_size_sampled():
+    w = W.sweep(dtype="bf16", hidden=2048, head_dim=128, tokens=32768, device="cuda")
+    g = torch.Generator().manual_seed(3)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, 32766, 32767]),
+                                   torch.randint(0, 32768, (60,), generator=g)]))
+    kv_parity(w, seq_idx=[0] * 32768, slot=list(range(32768)), n_seqs=1, max_seq=32768,
+              tag="kv/32k", rows=rows)
