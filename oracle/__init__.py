@@ -37,11 +37,14 @@ def lib():
         L.oracle_mrope.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int,
                                    _i64, _i64, _int, _int, _int, _dbl, _int]
         L.oracle_swiglu.argtypes = [_vp, _vp, _i64, _i64, _i64, _int]
+        L.oracle_softmax_topk_sample.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _dbl,
+                                                 _i64, _vp, _int]
         L.oracle_mrope_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int,
                                              _int, _int, _i64, _i64, _i64, _int, _int, _int, _dbl,
                                              _vp, _vp, _i64, _i64, _int]
         for f in ("oracle_round", "oracle_widen", "oracle_rmsnorm", "oracle_add_rmsnorm",
-                  "oracle_mrope", "oracle_swiglu", "oracle_mrope_kv_append"):
+                  "oracle_mrope", "oracle_swiglu", "oracle_mrope_kv_append",
+                  "oracle_softmax_topk_sample"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -149,6 +152,25 @@ def mrope_kv_append(q, k, v, pos, sections, theta, seq_idx, slot, k_cache, v_cac
                                  st, sh, sw, float(theta), _ptr(seq_idx), _ptr(slot), n_seqs, max_seq,
                                  _code(q))
     return qo, kc, vc
+
+
+def softmax_topk_sample(logits: torch.Tensor, temperature: float, top_k: int, u, want_probs=True):
+    """logits: [rows, vocab] (row stride free); u: [rows] float32 uniforms.
+    Returns (token int32 [rows], probs float64 [rows, vocab] or None,
+    kept int64 [rows, top_k], cdf float64 [rows, top_k])."""
+    x = _cpu(logits)
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, vocab = x.shape
+    assert 1 <= top_k <= vocab
+    uu = np.ascontiguousarray(np.asarray(u, dtype=np.float32).reshape(rows))
+    tok = np.empty(rows, dtype=np.int32)
+    probs = np.empty((rows, vocab), dtype=np.float64) if want_probs else None
+    kept = np.empty((rows, top_k), dtype=np.int64)
+    cdf = np.empty((rows, top_k), dtype=np.float64)
+    lib().oracle_softmax_topk_sample(_ptr(tok), None if probs is None else _ptr(probs), _ptr(kept),
+                                     _ptr(cdf), _ptr(x), rows, vocab, x.stride(0),
+                                     float(temperature), int(top_k), _ptr(uu), _code(x))
+    return tok, probs, kept, cdf
 
 
 def swiglu(gate_up: torch.Tensor) -> np.ndarray:

@@ -32,6 +32,8 @@
  *     silu(g) = g * sigmoid(g).
  *   - KV-cache append: one cache [n_kv][max_seq][head_dim] per sequence; each
  *     token names its sequence and slot; out-of-range tokens write nothing.
+ *   - Softmax + top-k sampling: top_k largest logits (lower index on ties),
+ *     renormalised, inverse-CDF sample with a caller-supplied uniform.
  *
  * Parity pins live in the CPU tests (closed forms, invariants, library
  * routines, a hand example); no function here is "parity unpinned".
@@ -244,6 +246,89 @@ void oracle_mrope_kv_append(double *q_out, double *k_cache_out, void *v_cache,
         }
     }
     free(k_rot);
+}
+
+/* Order of two candidates for top-k: larger logit first, lower index on a tie. */
+static const double *g_topk_vals;
+static int topk_order(const void *a, const void *b)
+{
+    const int64_t i = *(const int64_t *)a, j = *(const int64_t *)b;
+    const double x = g_topk_vals[i], y = g_topk_vals[j];
+    if (x > y) {
+        return -1;
+    }
+    if (x < y) {
+        return 1;
+    }
+    return i < j ? -1 : (i > j ? 1 : 0);
+}
+
+/* [P1] "Custom Triton kernels", kernel 2 (fused softmax + top-K sampling):
+ * probs = softmax(logits / temperature) over the vocabulary (the page divides
+ * by the temperature, subtracts the max, exponentiates and normalises; its
+ * top-K and sampling steps are cut off).  Reading for the missing steps: keep
+ * the top_k largest logits (lower index first on ties), renormalise their
+ * probabilities, and return the first kept token, in that order, whose
+ * cumulative probability exceeds u[row] (the last kept token if rounding
+ * leaves none).  probs (double, [rows][vocab]) may be NULL.  For the parity
+ * check, kept[row][top_k] receives the kept tokens in order and cdf[row][top_k]
+ * their exact cumulative probabilities (both may be NULL). */
+void oracle_softmax_topk_sample(int32_t *token, double *probs, int64_t *kept, double *cdf,
+                                const void *logits, int64_t rows, int64_t vocab,
+                                int64_t row_stride, double temperature, int64_t top_k,
+                                const float *u, int dtype)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)vocab);
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)vocab);
+    for (int64_t r = 0; r < rows; ++r) {
+        double zmax = -INFINITY;
+        for (int64_t i = 0; i < vocab; ++i) {
+            z[i] = widen(logits, r * row_stride + i, dtype) / temperature;
+            if (z[i] > zmax) {
+                zmax = z[i];
+            }
+        }
+        if (probs) {
+            double sum = 0.0;
+            for (int64_t i = 0; i < vocab; ++i) {
+                sum += exp(z[i] - zmax);
+            }
+            for (int64_t i = 0; i < vocab; ++i) {
+                probs[r * vocab + i] = exp(z[i] - zmax) / sum;
+            }
+        }
+        /* rank by the logits themselves: dividing by temperature > 0 keeps the order */
+        for (int64_t i = 0; i < vocab; ++i) {
+            order[i] = i;
+            z[i] = widen(logits, r * row_stride + i, dtype);
+        }
+        g_topk_vals = z;
+        qsort(order, (size_t)vocab, sizeof(int64_t), topk_order);
+        const double zt = z[order[0]] / temperature;
+        double kept_sum = 0.0;
+        for (int64_t j = 0; j < top_k; ++j) {
+            kept_sum += exp(z[order[j]] / temperature - zt);
+        }
+        double cum = 0.0;
+        int32_t pick = (int32_t)order[top_k - 1];
+        int found = 0;
+        for (int64_t j = 0; j < top_k; ++j) {
+            cum += exp(z[order[j]] / temperature - zt) / kept_sum;
+            if (kept) {
+                kept[r * top_k + j] = order[j];
+            }
+            if (cdf) {
+                cdf[r * top_k + j] = cum;
+            }
+            if (!found && cum > (double)u[r]) {
+                pick = (int32_t)order[j];
+                found = 1;
+            }
+        }
+        token[r] = pick;
+    }
+    free(order);
+    free(z);
 }
 
 /* sigmoid, evaluated so that exp never overflows: 1/(1+e^-g) for g >= 0 and

@@ -44,6 +44,13 @@ void oracle_mrope_kv_append(double *q_out, double *k_cache_out, void *v_cache,
                             int sec_w, double theta, const int32_t *seq_idx, const int32_t *slot,
                             int64_t n_seqs, int64_t max_seq, int dtype);
 
+/* token[rows]; probs[rows][vocab] (double, may be NULL); kept/cdf [rows][top_k]
+ * (may be NULL); u[rows] uniforms in [0, 1). */
+void oracle_softmax_topk_sample(int32_t *token, double *probs, int64_t *kept, double *cdf,
+                                const void *logits, int64_t rows, int64_t vocab,
+                                int64_t row_stride, double temperature, int64_t top_k,
+                                const float *u, int dtype);
+
 /* out[rows][inter] (double) from gate_up rows [gate | up] of stride gate_up_stride. */
 void oracle_swiglu(double *out, const void *gate_up, int64_t rows, int64_t inter,
                    int64_t gate_up_stride, int dtype);

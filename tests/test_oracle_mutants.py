@@ -37,6 +37,13 @@ MUTANTS = [
     ("sigmoid_sign", "return 1.0 / (1.0 + exp(-g));", "return 1.0 / (1.0 + exp(g));"),
     ("naive_sigmoid_underflow", "double e = exp(g);\n    return e / (1.0 + e);", "return (float)(1.0 / (1.0 + exp(-(double)(float)g)));"),
     ("bf16_truncates", "nearbyint(a / quantum)", "floor(a / quantum)"),
+    ("topk_ascending", "    if (x > y) {\n        return -1;\n    }\n    if (x < y) {\n        return 1;\n    }",
+     "    if (x > y) {\n        return 1;\n    }\n    if (x < y) {\n        return -1;\n    }"),
+    ("topk_ties_high_index_first", "return i < j ? -1 : (i > j ? 1 : 0);", "return i < j ? 1 : (i > j ? -1 : 0);"),
+    ("topk_not_renormalised", "cum += exp(z[order[j]] / temperature - zt) / kept_sum;",
+     "cum += exp(z[order[j]] / temperature - zt) / (kept_sum * 1.25);"),
+    ("topk_sample_ge", "if (!found && cum > (double)u[r]) {", "if (!found && cum >= (double)u[r]) {"),
+    ("topk_temperature_ignored", "const double zt = z[order[0]] / temperature;", "const double zt = z[order[0]]; temperature = 1.0;"),
     ("kv_seq_head_swapped", "const int64_t at = ((b * n_kv_heads + h) * max_seq + s) * head_dim;",
      "const int64_t at = ((h * n_seqs + b) * max_seq + s) * head_dim;"),
     ("kv_cache_gets_unrotated_k", "k_cache_out[at + d] = k_rot[h * head_dim + d];",

@@ -421,3 +421,60 @@ def test_kv_append_rotates_like_mrope_and_skips_out_of_range():
                 if untouched[b, s_]:
                     assert np.all(kc2[b, :, s_] == -7.0)
                     assert torch.all(vc2[b, :, s_] == torch.tensor(-3.0).to(dt))
+
+
+# ----------------------------------------------------------------- softmax + top-k sampling
+
+def _sample(logits, T, k, u, dt=torch.float32):
+    x = torch.tensor(np.atleast_2d(np.asarray(logits, dtype=np.float32))).to(dt)
+    return oracle.softmax_topk_sample(x, T, k, np.atleast_1d(np.asarray(u, dtype=np.float32)))
+
+
+def test_topk_sample_closed_form():
+    # logits 0..3, T = 1, k = 2: kept (3, 2) with probabilities e^3 : e^2, so
+    # the first cumulative probability is e/(e+1) = sigmoid(1)
+    s1 = 1.0 / (1.0 + math.exp(-1.0))
+    tok, probs, kept, cdf = _sample([0, 1, 2, 3], 1.0, 2, 0.7)
+    assert kept[0].tolist() == [3, 2] and tok[0] == 3
+    assert cdf[0, 0] == pytest.approx(s1, rel=1e-15) and cdf[0, 1] == pytest.approx(1.0, rel=1e-15)
+    assert _sample([0, 1, 2, 3], 1.0, 2, 0.75)[0][0] == 2
+    e = np.exp(np.arange(4.0))
+    np.testing.assert_allclose(probs[0], e / e.sum(), rtol=1e-15)
+    # temperature 2 halves the logits: 0 and 2 -> sigmoid(1) again
+    tok, _, kept, cdf = _sample([0, 2], 2.0, 2, 0.7)
+    assert kept[0].tolist() == [1, 0] and tok[0] == 1
+    assert cdf[0, 0] == pytest.approx(s1, rel=1e-15)
+
+
+def test_topk_sample_ties_and_boundaries():
+    tok, _, kept, _ = _sample([1, 5, 5, 5, 0], 1.0, 2, 0.1)
+    assert kept[0].tolist() == [1, 2]                  # equal logits: lower index first
+    # u exactly at a cumulative probability: the next token (strictly greater)
+    tok, _, kept, cdf = _sample([0, 0], 1.0, 2, 0.5)
+    assert cdf[0, 0] == 0.5 and tok[0] == 1
+    assert _sample([0, 0], 1.0, 2, 0.4999)[0][0] == 0
+    # k = 1 is greedy whatever u is; u near 1 takes the last kept token
+    for u in (0.0, 0.3, 0.999999):
+        assert _sample([0.5, 3.0, -1.0, 3.0], 0.7, 1, u)[0][0] == 1
+    assert _sample([0, 1, 2, 3], 1.0, 3, 0.9999999)[0][0] == 1
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 1.7])
+def test_topk_sample_matches_torch_softmax_and_topk(T):
+    x = torch.from_numpy(rng.standard_normal((4, 3000)).astype(np.float32) * 4)
+    tok, probs, kept, cdf = oracle.softmax_topk_sample(x, T, 50, rng.random(4).astype(np.float32))
+    np.testing.assert_allclose(probs, torch.softmax(x.double() / T, dim=1).numpy(), rtol=1e-12)
+    tk = torch.topk(x.double(), 50, dim=1, sorted=True).indices.numpy()
+    assert np.array_equal(kept, tk)
+    ren = np.take_along_axis(probs, kept, axis=1)
+    np.testing.assert_allclose(cdf, np.cumsum(ren / ren.sum(axis=1, keepdims=True), axis=1), rtol=1e-12)
+
+
+def test_topk_sample_inverse_cdf_frequencies():
+    # stratified uniforms (i + 1/2)/N: token j must be drawn N * p_j +- 1 times
+    x = torch.from_numpy(rng.standard_normal(64).astype(np.float32) * 2)
+    N = 20000
+    u = (np.arange(N) + 0.5) / N
+    tok, probs, _, _ = oracle.softmax_topk_sample(x.repeat(N, 1), 1.0, 64, u.astype(np.float32))
+    counts = np.bincount(tok, minlength=64)
+    assert np.all(np.abs(counts - N * probs[0]) <= 1.5)
