@@ -302,9 +302,22 @@ def main():
     vc = torch.empty_like(kc)
     seq0 = torch.zeros(T, dtype=torch.int32, device=dev)
     slots = torch.arange(T, dtype=torch.int32, device=dev)
-    nxt = {"mrope_kv_append": lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
-                                                          kc, vc, seq0, slots)}
-    for op, fn in nxt.items():
+    # sampling: the decode step's 5 candidates over a 3072-entry codec vocabulary, and a
+    # text-sized vocabulary at 256 rows (algorithmic bytes: logits read once, u, token)
+    lg_dec = torch.randn(5, 3072, device=dev).mul_(4.0).to(torch.bfloat16)
+    lg_big = torch.randn(256, 151936, device=dev).mul_(3.0).to(torch.bfloat16)
+    u5, u256 = torch.rand(5, device=dev), torch.rand(256, device=dev)
+    tok5 = torch.empty(5, dtype=torch.int32, device=dev)
+    tok256 = torch.empty(256, dtype=torch.int32, device=dev)
+    nxt = {"mrope_kv_append": (lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
+                                                           kc, vc, seq0, slots),
+                               algorithmic_bytes("mrope_kv_append", T, H, I, nq, nkv, D, s)),
+           "softmax_topk_sample_5x3072_k50": (
+               lambda: nrs.softmax_topk_sample(lg_dec, 0.9, 50, u5, token=tok5), 5 * 3072 * 2 + 5 * 8),
+           "softmax_topk_sample_256x151936_k50": (
+               lambda: nrs.softmax_topk_sample(lg_big, 1.0, 50, u256, token=tok256),
+               256 * 151936 * 2 + 256 * 8)}
+    for op, (fn, byts) in nxt.items():
         for _ in range(3):
             fn()
         reps = []
@@ -317,11 +330,10 @@ def main():
             torch.cuda.synchronize()
             reps.append(1e3 * a.elapsed_time(b) / K)
         mean_us = sum(reps) / NREP
-        byts = algorithmic_bytes(op, T, H, I, nq, nkv, D, s)
         next_ops[op] = {"mean_us": round(mean_us, 2), "bytes": byts,
                         "GB_s": round(byts / (mean_us * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(byts / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    del v, kc, vc
+    del v, kc, vc, lg_dec, lg_big
     print(f"bench: next {json.dumps(next_ops)}", file=sys.stderr, flush=True)
 
     sw = per_op["swiglu"]

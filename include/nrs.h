@@ -150,6 +150,29 @@ int nrs_mrope_kv_append(void *q, const void *k, const void *v, const int32_t *po
 int nrs_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
                int64_t gate_up_stride, int64_t out_stride, int dtype, void *stream);
 
+/*
+ * Fused softmax + top-k sampling over vocabulary logits.  [P1] "Custom Triton
+ * kernels", kernel 2: softmax(logits / temperature) then sampling in one
+ * pass over the row (the page's sketch stops after the softmax; its top-k and
+ * sampling steps are completed as follows).  Per row: keep the top_k largest
+ * logits (lower index first on equal logits), renormalise their probabilities,
+ * and write to token[row] the first kept index, in that order, whose
+ * cumulative probability exceeds u[row] (the last kept index if rounding
+ * leaves none).
+ *   logits[rows][row_stride]: vocab values per row; vocab a multiple of 8
+ *     (bf16) or 4 (fp32), below 2^31.
+ *   u[rows]: fp32 uniforms in [0, 1) chosen by the caller (device array).
+ *   token[rows]: int32 output.
+ *   probs[rows][probs_stride]: optional (NULL: not written) softmax over the
+ *     whole row at this temperature, in the logits' type.
+ *   top_k: 1..1024 and <= vocab; temperature finite and > 0 (NRS_ERR_ARG).
+ * NaN logits give an unspecified token.
+ */
+int nrs_softmax_topk_sample(int32_t *token, void *probs, const void *logits, int64_t rows,
+                            int64_t vocab, int64_t row_stride, int64_t probs_stride,
+                            float temperature, int32_t top_k, const float *u, int dtype,
+                            void *stream);
+
 /* ---------------------------------------------------------------------------
  * Decode-step graphs.  [P2] part 3 ("Hybrid" note) replays the decode step as
  * a CUDA graph on top of the fused kernels; here the per-layer op set is

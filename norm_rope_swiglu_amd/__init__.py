@@ -3,7 +3,7 @@ RMSNorm, M-RoPE, SwiGLU) as hand-written HIP kernels for gfx950 behind a C
 ABI (include/nrs.h), with a thin torch-tensor binding."""
 from ._native import NrsError, lib
 from .ops import (Graph, add_rmsnorm, decode_graph, mrope, mrope_kv_append, null_graph, rmsnorm,
-                  swiglu)
+                  softmax_topk_sample, swiglu)
 
 __all__ = ["NrsError", "lib", "Graph", "add_rmsnorm", "decode_graph", "mrope", "mrope_kv_append",
-           "null_graph", "rmsnorm", "swiglu"]
+           "null_graph", "rmsnorm", "softmax_topk_sample", "swiglu"]

@@ -54,6 +54,8 @@ SIGNATURES = {
                                    _i64, _i32, _i32, _i32, _f64, _vp, _vp, _vp, _vp, _i64, _i64,
                                    _int, _vp]),
     "nrs_swiglu": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+    "nrs_softmax_topk_sample": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i32, _vp, _int,
+                                       _vp]),
     "nrs_decode_graph_create": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(DecodeShape),
                                        ctypes.POINTER(DecodeLayer), _i32]),
     "nrs_null_graph_create": (_int, [ctypes.POINTER(_vp), _i32]),

@@ -175,6 +175,19 @@ NRS_API int nrs_swiglu(void *out, const void *gate_up, int64_t rows, int64_t int
                                          dtype, (hipStream_t)stream));
 }
 
+NRS_API int nrs_softmax_topk_sample(int32_t *token, void *probs, const void *logits, int64_t rows,
+                                    int64_t vocab, int64_t row_stride, int64_t probs_stride,
+                                    float temperature, int32_t top_k, const float *u, int dtype,
+                                    void *stream) {
+    int st = nrs::check_topk_sample(token, probs, logits, rows, vocab, row_stride, probs_stride,
+                                    temperature, top_k, u, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    clear_stale_error();
+    return hip_status(nrs::launch_topk_sample(token, probs, logits, rows, vocab, row_stride,
+                                              probs_stride, temperature, top_k, u, dtype,
+                                              (hipStream_t)stream));
+}
+
 NRS_API int nrs_decode_graph_create(nrs_graph *out, const nrs_decode_shape *shape,
                                     const nrs_decode_layer *layers, int32_t n_layers) {
     if (!out || !shape || (n_layers > 0 && !layers)) return NRS_ERR_NULL;

@@ -38,6 +38,10 @@ hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t 
                            int64_t n_seqs, int64_t max_seq, int dtype, hipStream_t stream);
 hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t inter,
                          int64_t gu_stride, int64_t out_stride, int dtype, hipStream_t stream);
+hipError_t launch_topk_sample(int32_t *token, void *probs, const void *logits, int64_t rows,
+                              int64_t vocab, int64_t row_stride, int64_t probs_stride,
+                              float temperature, int32_t top_k, const float *u, int dtype,
+                              hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);
 
 }  // namespace nrs

@@ -1,0 +1,310 @@
+// Fused softmax + top-k sampling over vocabulary logits, gfx950.
+//
+// "Optimising autoregressive speech models", "Custom Triton kernels", kernel 2:
+// decoding ends with softmax then sampling, and fusing them saves a full
+// write and re-read of the vocabulary row.  The page's sketch divides the
+// logits by the temperature, subtracts the max, exponentiates and normalises;
+// its top-k and sampling steps are cut off.  Completed here as: keep the
+// top_k largest logits (lower index first on ties), renormalise their
+// probabilities, and return the first kept token, in that order, whose
+// cumulative probability exceeds the caller's uniform u[row] (the last kept
+// token if rounding leaves none).  The full softmax row is written only when
+// asked for.
+//
+// One 1024-thread workgroup per row:
+//   1. radix select of the k-th largest logit on monotone 32-bit keys, 8 bits
+//      per pass (4 passes for fp32, 2 for bf16, whose low 16 key bits are
+//      fixed by the sign), histograms in LDS;
+//   2. an ordered compaction pass gathers every logit above that key and the
+//      lowest-index ties (a block-wide prefix count keeps ties in index order);
+//   3. a bitonic sort of the (at most 1024) kept entries in LDS by (logit
+//      descending, index ascending);
+//   4. exp((l - l_max) / T) per kept entry, an inclusive block scan, and the
+//      first entry whose prefix exceeds u * total.
+// Every pass reads the row with 16-byte loads; the row is re-read from the
+// caches between passes.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace nrs {
+
+namespace {
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;  // chunks in flight per thread in the passes over the row
+
+// Order-preserving map of an fp32 value to uint32 (larger value, larger key);
+// -0 is folded onto +0 so equal values have equal keys.
+__device__ inline uint32_t key_of(float f) {
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline float value_of(uint32_t k) {
+    const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __builtin_bit_cast(float, b);
+}
+
+// Exclusive prefix over the block (thread order) of a small int, and the total.
+__device__ inline int block_exclusive_scan(int v, int *wave_tot, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int t = wave_tot[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Inclusive prefix sum over the block (thread order) of a float.
+__device__ inline float block_inclusive_scan(float v, float *wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    float before = 0.0f;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    __syncthreads();
+    return before + incl;
+}
+}  // namespace
+
+template <typename IO>
+__global__ __launch_bounds__(kThreads) void topk_sample_kernel(
+    int32_t *token, IO *probs, const IO *logits, int64_t vocab, int64_t row_stride,
+    int64_t probs_stride, float inv_temp, int32_t top_k, const float *u) {
+    using T = io_traits<IO>;
+    constexpr int VEC = T::VEC;
+    constexpr int NPASS = sizeof(IO) == 4 ? 4 : 2;
+    __shared__ uint32_t hist[256 * 32];   // 256 digits x 32 bank replicas
+    __shared__ uint32_t wtot[4];
+    __shared__ uint32_t sel[2];            // selected digit, count strictly above it
+    __shared__ int iscan[kWaves];
+    __shared__ float fscan[kWaves];
+    __shared__ uint32_t ckey[kThreads];    // kept entries: key and index
+    __shared__ int32_t cidx[kThreads];
+    __shared__ float csum[kThreads];       // prefix sums of the kept weights
+    __shared__ uint32_t n_gt;
+    __shared__ int32_t pick;
+
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const IO *x = logits + row * row_stride;
+    const int64_t nchunks = vocab / VEC;
+
+    // 1. radix select: find the top_k-th largest key.  Each bin is replicated
+    //    across the 32 LDS banks (indexed by lane) so lanes counting the same
+    //    digit, common with peaky logits, rarely hit one address.
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t need = (uint32_t)top_k;
+    const uint32_t rep = tid & 31;
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256 * 32; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        for (int64_t c0 = tid; c0 < nchunks; c0 += kUnroll * kThreads) {
+            u32x4 raw[kUnroll];
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j) {
+                const int64_t c = c0 + j * kThreads;
+                if (c < nchunks) raw[j] = load16(x + c * VEC);
+            }
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j) {
+                if (c0 + j * kThreads >= nchunks) break;
+                float v[VEC];
+                T::unpack(raw[j], v);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const uint32_t key = key_of(v[e]);
+                    if ((key & pmask) == prefix)
+                        atomicAdd(&hist[((key >> shift) & 255u) * 32 + rep], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        // thread t < 256 sums digit 255 - t (rotating the replica index keeps
+        // the 64 lanes of a wave on different banks); an inclusive scan over t
+        // then counts the candidates with digit >= 255 - t: per wave first,
+        // then, after a barrier every thread reaches, across the four waves
+        const uint32_t d = 255u - (uint32_t)(tid & 255);
+        uint32_t h = 0, incl = 0;
+        if (tid < 256) {
+            for (int r = 0; r < 32; ++r) h += hist[d * 32 + ((r + tid) & 31)];
+            incl = h;
+            const int lane = tid & 63;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t up = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += up;
+            }
+            if (lane == 63) wtot[tid >> 6] = incl;
+        }
+        __syncthreads();
+        if (tid < 256) {
+            for (int w2 = 0; w2 < (tid >> 6); ++w2) incl += wtot[w2];
+            if (incl - h < need && need <= incl) {  // the need-th largest has digit d
+                sel[0] = d;
+                sel[1] = incl - h;
+            }
+        }
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        pmask |= 255u << shift;
+        need -= sel[1];
+        __syncthreads();
+    }
+    // keys below the selected passes are fixed (bf16: the low 16 bits follow
+    // the sign), so one representative key decides the comparisons
+    const uint32_t kth = prefix;
+    const uint32_t kth_mask = pmask;
+    const int n_above = top_k - (int)need;   // keys strictly above kth
+
+    // 2. ordered compaction of the kept entries
+    if (tid == 0) n_gt = 0;
+    __syncthreads();
+    int eq_taken = 0;
+    for (int64_t base = 0; base < nchunks; base += kThreads) {
+        const int64_t c = base + tid;
+        float v[VEC];
+        int n_eq = 0;
+        if (c < nchunks) {
+            T::unpack(load16(x + c * VEC), v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t key = key_of(v[e]) & kth_mask;
+                if (key > kth) {
+                    const uint32_t at = atomicAdd(&n_gt, 1u);
+                    ckey[at] = key_of(v[e]);
+                    cidx[at] = (int32_t)(c * VEC + e);
+                } else if (key == kth) {
+                    ++n_eq;
+                }
+            }
+        }
+        int chunk_total;
+        int r = eq_taken + block_exclusive_scan(n_eq, iscan, chunk_total);
+        if (c < nchunks && n_eq > 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if ((key_of(v[e]) & kth_mask) == kth) {
+                    if (r < (int)need) {
+                        ckey[n_above + r] = key_of(v[e]);
+                        cidx[n_above + r] = (int32_t)(c * VEC + e);
+                    }
+                    ++r;
+                }
+            }
+        }
+        eq_taken += chunk_total;
+    }
+    __syncthreads();
+
+    // 3. bitonic sort of the kept entries: logit descending, index ascending
+    int n = 1;
+    while (n < top_k) n <<= 1;
+    if (tid >= top_k && tid < n) {
+        ckey[tid] = 0u;          // below every real key
+        cidx[tid] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (tid < n) {
+                const int other = tid ^ stride;
+                if (other > tid) {
+                    const uint32_t ka = ckey[tid], kb = ckey[other];
+                    const int32_t ia = cidx[tid], ib = cidx[other];
+                    const bool a_first = ka > kb || (ka == kb && ia < ib);
+                    const bool up = (tid & size) == 0;
+                    if (up != a_first) {
+                        ckey[tid] = kb;
+                        ckey[other] = ka;
+                        cidx[tid] = ib;
+                        cidx[other] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 4. renormalised weights of the kept entries, prefix sums, inverse CDF
+    const float lmax = value_of(ckey[0]);
+    const float w = tid < top_k ? expf((value_of(ckey[tid]) - lmax) * inv_temp) : 0.0f;
+    const float cum = block_inclusive_scan(w, fscan);
+    csum[tid] = cum;
+    if (tid == 0) pick = -1;
+    __syncthreads();
+    // the prefixes are non-decreasing, so exactly one kept entry has
+    // prefix > u * total >= the previous prefix, unless rounding leaves
+    // u * total at or above the last prefix
+    const float thr = u[row] * csum[top_k - 1];
+    const float before = tid > 0 ? csum[tid - 1] : 0.0f;
+    if (tid < top_k && cum > thr && (tid == 0 || before <= thr)) pick = cidx[tid];
+    __syncthreads();
+    if (tid == 0) token[row] = pick >= 0 ? pick : cidx[top_k - 1];
+
+    // optional full softmax row
+    if (probs) {
+        float part = 0.0f;
+        for (int64_t c = tid; c < nchunks; c += kThreads) {
+            float v[VEC];
+            T::unpack(load16(x + c * VEC), v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) part += expf((v[e] - lmax) * inv_temp);
+        }
+        part = wave_sum(part);
+        if ((tid & 63) == 0) fscan[tid >> 6] = part;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) tot += fscan[wv];
+        const float inv = 1.0f / tot;
+        IO *p = probs + row * probs_stride;
+        for (int64_t c = tid; c < nchunks; c += kThreads) {
+            float v[VEC], o[VEC];
+            T::unpack(load16(x + c * VEC), v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = expf((v[e] - lmax) * inv_temp) * inv;
+            store16(p + c * VEC, T::pack(o));
+        }
+    }
+}
+
+hipError_t launch_topk_sample(int32_t *token, void *probs, const void *logits, int64_t rows,
+                              int64_t vocab, int64_t row_stride, int64_t probs_stride,
+                              float temperature, int32_t top_k, const float *u, int dtype,
+                              hipStream_t stream) {
+    const dim3 grid((unsigned)rows), block(kThreads);
+    const float inv_temp = (float)(1.0 / (double)temperature);
+    if (dtype == 0)
+        hipLaunchKernelGGL(topk_sample_kernel<float>, grid, block, 0, stream, token,
+                           (float *)probs, (const float *)logits, vocab, row_stride, probs_stride,
+                           inv_temp, top_k, u);
+    else
+        hipLaunchKernelGGL(topk_sample_kernel<__bf16>, grid, block, 0, stream, token,
+                           (__bf16 *)probs, (const __bf16 *)logits, vocab, row_stride,
+                           probs_stride, inv_temp, top_k, u);
+    return hipGetLastError();
+}
+
+}  // namespace nrs

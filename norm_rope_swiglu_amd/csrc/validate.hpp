@@ -108,4 +108,23 @@ inline int check_swiglu(const void *out, const void *gate_up, int64_t rows, int6
     return NRS_OK;
 }
 
+constexpr int kMaxTopK = 1024;
+
+inline int check_topk_sample(const int32_t *token, const void *probs, const void *logits,
+                             int64_t rows, int64_t vocab, int64_t row_stride, int64_t probs_stride,
+                             float temperature, int32_t top_k, const float *u, int dtype) {
+    if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
+    if (rows < 0 || vocab <= 0 || vocab % vec_of(dtype) != 0 || vocab >= ((int64_t)1 << 31))
+        return NRS_ERR_SHAPE;
+    if (top_k < 1 || top_k > kMaxTopK || top_k > vocab) return NRS_ERR_ARG;
+    if (!(temperature > 0.0f) || isinf(temperature)) return NRS_ERR_ARG;
+    if (rows == 0) return NRS_OK;
+    if (row_stride < vocab || (probs && probs_stride < vocab)) return NRS_ERR_SHAPE;
+    if (!token || !logits || !u) return NRS_ERR_NULL;
+    if (!aligned16(logits) || !stride_ok(row_stride, dtype) || ((uintptr_t)token & 3u) ||
+        ((uintptr_t)u & 3u) || (probs && (!aligned16(probs) || !stride_ok(probs_stride, dtype))))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
 }  // namespace nrs

@@ -188,6 +188,35 @@ def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
     return out
 
 
+def softmax_topk_sample(logits: torch.Tensor, temperature: float, top_k: int, u: torch.Tensor,
+                        token: torch.Tensor | None = None, probs: torch.Tensor | bool = False):
+    """Sample one token per row of logits [rows, vocab] from the renormalised
+    top_k softmax at `temperature`, using the caller's uniforms u [rows]
+    (float32).  Returns token (int32 [rows]), or (token, probs) when probs is
+    True or a tensor to fill with the full softmax."""
+    lg = _rows2d(logits, "logits")
+    rows, vocab = lg.shape
+    if u.dtype != torch.float32 or u.shape != (rows,) or not u.is_contiguous():
+        raise ValueError("u must be contiguous float32 [rows]")
+    if token is None:
+        token = torch.empty(rows, dtype=torch.int32, device=lg.device)
+    if token.dtype != torch.int32 or token.shape != (rows,) or not token.is_contiguous():
+        raise ValueError("token must be contiguous int32 [rows]")
+    want = probs is not False
+    if probs is True:
+        probs = torch.empty_like(lg)
+    p2 = _rows2d(probs, "probs") if want else None
+    if want and p2.shape != lg.shape:
+        raise ValueError("probs must match logits")
+    d = _dev(lg, u, token, *((p2,) if want else ()))
+    with _on(d):
+        check(lib().nrs_softmax_topk_sample(
+            token.data_ptr(), p2.data_ptr() if want else None, lg.data_ptr(), rows, vocab,
+            lg.stride(0), p2.stride(0) if want else 0, float(temperature), int(top_k),
+            u.data_ptr(), _code(lg), _stream(d)), "nrs_softmax_topk_sample")
+    return (token, probs) if want else token
+
+
 class Graph:
     """A recorded hipGraph; holds references to every tensor it binds."""
 

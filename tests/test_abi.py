@@ -172,6 +172,33 @@ def test_mrope_kv_append_rejects(L, args, want):
     assert L.nrs_mrope_kv_append(*args, None) == want
 
 
+TS = [  # (token, probs, logits, rows, vocab, row_stride, probs_stride, temperature, top_k, u, dtype)
+    ((P, None, P, 4, 3072, 3072, 0, 1.0, 50, P, 2), DTYPE),
+    ((P, None, P, -1, 3072, 3072, 0, 1.0, 50, P, 1), SHAPE),
+    ((P, None, P, 4, 3070, 3070, 0, 1.0, 50, P, 1), SHAPE),       # not a multiple of 8 bf16
+    ((P, None, P, 4, 3072, 3072, 0, 1.0, 0, P, 1), ARG),
+    ((P, None, P, 4, 3072, 3072, 0, 1.0, 1025, P, 1), ARG),
+    ((P, None, P, 4, 16, 16, 0, 1.0, 17, P, 1), ARG),             # top_k > vocab
+    ((P, None, P, 4, 3072, 3072, 0, 0.0, 50, P, 1), ARG),
+    ((P, None, P, 4, 3072, 3072, 0, float("inf"), 50, P, 1), ARG),
+    ((P, None, P, 4, 3072, 3000, 0, 1.0, 50, P, 1), SHAPE),
+    ((P, P, P, 4, 3072, 3072, 100, 1.0, 50, P, 1), SHAPE),
+    ((None, None, P, 4, 3072, 3072, 0, 1.0, 50, P, 1), NULL),
+    ((P, None, None, 4, 3072, 3072, 0, 1.0, 50, P, 1), NULL),
+    ((P, None, P, 4, 3072, 3072, 0, 1.0, 50, None, 1), NULL),
+    ((P + 2, None, P, 4, 3072, 3072, 0, 1.0, 50, P, 1), ALIGN),
+    ((P, None, U, 4, 3072, 3072, 0, 1.0, 50, P, 1), ALIGN),
+    ((P, None, P, 4, 3072, 3076, 0, 1.0, 50, P, 1), ALIGN),
+    ((P, U, P, 4, 3072, 3072, 3072, 1.0, 50, P, 1), ALIGN),
+    ((None, None, None, 0, 3072, 3072, 0, 1.0, 50, None, 1), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", TS)
+def test_softmax_topk_sample_rejects(L, args, want):
+    assert L.nrs_softmax_topk_sample(*args, None) == want
+
+
 SWIGLU = [  # (out, gate_up, rows, inter, gate_up_stride, out_stride, dtype)
     ((P, P, 4, 768, 1536, 768, 9), DTYPE),
     ((P, P, -2, 768, 1536, 768, 1), SHAPE),

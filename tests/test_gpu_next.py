@@ -1,5 +1,6 @@
 """GPU parity of the ops beyond the four-op hot path, through the C ABI,
-against the fp64 oracle: M-RoPE fused with the KV-cache append."""
+against the fp64 oracle: M-RoPE fused with the KV-cache append, and fused
+softmax + top-k sampling."""
 from __future__ import annotations
 
 import numpy as np
@@ -123,3 +124,79 @@ def test_kv_append_full_size_sampled():
                                    torch.randint(0, 32768, (60,), generator=g)]))
     kv_parity(w, seq_idx=[0] * 32768, slot=list(range(32768)), n_seqs=1, max_seq=32768,
               tag="kv/32k", rows=rows)
+
+
+# ------------------------------------------------------------ fused softmax + top-k sampling
+
+DELTA = 1e-5   # fp32 prefix-sum error allowance on the sampling CDF (k <= 1024 terms)
+
+
+def _logits(rows, vocab, scale, dt, seed, ties=False):
+    key = W.stream_key(seed, f"logits/{rows}/{vocab}/{scale}/{ties}")
+    v = W.normal(key, rows * vocab).reshape(rows, vocab) * scale
+    if ties:
+        v = torch.round(v)
+    return W.store(v, dt)
+
+
+def _u(rows, seed):
+    return W.uniform(W.stream_key(seed, f"u/{rows}"), rows).to(torch.float32)
+
+
+def sample_parity(logits, T, k, u, tag):
+    """Check the full softmax, and that every sampled token lies in the
+    oracle's kept set with u inside its exact CDF interval (to DELTA); where u
+    is farther than DELTA from every boundary the token must be the oracle's."""
+    tok, probs = nrs.softmax_topk_sample(logits.cuda(), T, k, u.cuda(), probs=True)
+    otok, oprobs, kept, cdf = oracle.softmax_topk_sample(logits, T, k, u.numpy())
+    check(f"{tag}/probs", probs, oprobs)
+    tok = tok.cpu().numpy()
+    uu = u.numpy().astype(np.float64)
+    for r in range(logits.shape[0]):
+        where = np.nonzero(kept[r] == tok[r])[0]
+        assert where.size == 1, f"{tag}: row {r} token {tok[r]} not in the oracle's top {k}"
+        j = int(where[0])
+        lo = cdf[r, j - 1] if j > 0 else 0.0
+        assert lo - DELTA <= uu[r] < cdf[r, j] + DELTA, f"{tag}: row {r} u {uu[r]} outside [{lo}, {cdf[r, j]})"
+        if np.min(np.abs(cdf[r] - uu[r])) > DELTA:
+            assert tok[r] == otok[r], f"{tag}: row {r}"
+    return tok, otok
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("vocab,k,scale,T", [(3072, 50, 4.0, 0.9), (3072, 1024, 0.5, 1.0),
+                                             (4104, 7, 2.0, 0.7), (8, 8, 1.0, 1.3),
+                                             (151936, 50, 3.0, 1.0)])
+def test_sample_decode_rows(dt, vocab, k, scale, T):
+    rows = 5 if vocab > 50000 else 33
+    lg = _logits(rows, vocab, scale, dt, 1)
+    sample_parity(lg, T, k, _u(rows, 2), f"sample/{dt}/V{vocab}/k{k}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_ties(dt):
+    # integer-valued logits: many equal values, the k-th often tied
+    lg = _logits(40, 3072, 2.0, dt, 3, ties=True)
+    sample_parity(lg, 1.0, 100, _u(40, 4), f"sample/ties/{dt}")
+    lg = torch.zeros(3, 1024).to(lg.dtype)                # all equal: lowest indices kept
+    tok, _ = sample_parity(lg, 1.0, 16, torch.tensor([0.0, 0.5, 0.99], dtype=torch.float32),
+                           f"sample/flat/{dt}")
+    assert tok.tolist() == [0, 8, 15]
+
+
+def test_sample_greedy_is_first_argmax():
+    lg = _logits(64, 3072, 4.0, "f32", 5)
+    lg[:, 1234] = lg.max(dim=1).values + 1.0
+    lg[:, 2222] = lg[:, 1234]                              # tied maximum: lower index wins
+    tok = nrs.softmax_topk_sample(lg.cuda(), 1.0, 1, _u(64, 6).cuda()).cpu()
+    assert torch.all(tok == 1234)
+
+
+def test_sample_inverse_cdf_frequencies():
+    lg = _logits(1, 64, 2.0, "f32", 7).repeat(20000, 1)
+    N = lg.shape[0]
+    u = ((torch.arange(N, dtype=torch.float64) + 0.5) / N).to(torch.float32)
+    tok = nrs.softmax_topk_sample(lg.cuda(), 1.0, 64, u.cuda()).cpu().numpy()
+    _, probs, _, _ = oracle.softmax_topk_sample(lg[:1], 1.0, 64, np.zeros(1, np.float32))
+    counts = np.bincount(tok, minlength=64)
+    assert np.all(np.abs(counts - N * probs[0]) <= 2.0)
