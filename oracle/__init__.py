@@ -34,6 +34,8 @@ def lib():
         L.oracle_widen.argtypes = [_vp, _vp, _i64, _int]
         L.oracle_rmsnorm.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _dbl, _int]
         L.oracle_add_rmsnorm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _dbl, _int]
+        L.oracle_layernorm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _dbl, _int]
+        L.oracle_add_layernorm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _dbl, _int]
         L.oracle_mrope.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int,
                                    _i64, _i64, _int, _int, _int, _dbl, _int]
         L.oracle_swiglu.argtypes = [_vp, _vp, _i64, _i64, _i64, _int]
@@ -44,7 +46,7 @@ def lib():
                                              _vp, _vp, _i64, _i64, _int]
         for f in ("oracle_round", "oracle_widen", "oracle_rmsnorm", "oracle_add_rmsnorm",
                   "oracle_mrope", "oracle_swiglu", "oracle_mrope_kv_append",
-                  "oracle_softmax_topk_sample"):
+                  "oracle_softmax_topk_sample", "oracle_layernorm", "oracle_add_layernorm"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -105,6 +107,34 @@ def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, ep
     res_out = torch.empty_like(x)
     lib().oracle_add_rmsnorm(_ptr(y), _ptr(res_out), _ptr(x), _ptr(residual), _ptr(g), rows,
                              hidden, float(eps), _code(x))
+    return y, res_out
+
+
+def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta, eps: float) -> np.ndarray:
+    """x: [rows, hidden] with unit column stride; beta may be None."""
+    x = _cpu(x)
+    assert x.dim() == 2 and x.stride(1) == 1 and gamma.dtype == x.dtype
+    rows, hidden = x.shape
+    g = _cpu(gamma).contiguous()
+    b = None if beta is None else _cpu(beta).contiguous()
+    assert b is None or b.dtype == x.dtype
+    y = np.empty((rows, hidden), dtype=np.float64)
+    lib().oracle_layernorm(_ptr(y), _ptr(x), _ptr(g), None if b is None else _ptr(b), rows, hidden,
+                           x.stride(0), float(eps), _code(x))
+    return y
+
+
+def add_layernorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, beta, eps: float):
+    """Returns (y float64 [rows, hidden], residual_out tensor in x's dtype)."""
+    x, residual = _cpu(x).contiguous(), _cpu(residual).contiguous()
+    assert x.shape == residual.shape and x.dtype == residual.dtype == gamma.dtype
+    rows, hidden = x.shape
+    g = _cpu(gamma).contiguous()
+    b = None if beta is None else _cpu(beta).contiguous()
+    y = np.empty((rows, hidden), dtype=np.float64)
+    res_out = torch.empty_like(x)
+    lib().oracle_add_layernorm(_ptr(y), _ptr(res_out), _ptr(x), _ptr(residual), _ptr(g),
+                               None if b is None else _ptr(b), rows, hidden, float(eps), _code(x))
     return y, res_out
 
 

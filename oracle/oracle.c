@@ -24,6 +24,8 @@
  *     straight to the storage type (RNE) with no fp32 step in between.
  *   - Norm+Residual: h = round_io(x + residual) is stored as residual_out and
  *     the norm sees that rounded h.
+ *   - LayerNorm: population variance about the row mean; beta optional; the
+ *     fused add variant stores and normalises the rounded h as above.
  *   - M-RoPE: half-split pairs (j, j + D/2); pairs [0, s_t) follow the
  *     temporal stream, [s_t, s_t+s_h) the height stream, the rest the width
  *     stream; frequency theta^(-2j/D) as in standard RoPE, same for all
@@ -146,6 +148,53 @@ void oracle_add_rmsnorm(double *y, void *residual_out, const void *x,
         }
     }
     oracle_rmsnorm(y, residual_out, gamma, rows, hidden, hidden, eps, dtype);
+}
+
+/* [P1] section 09, "What it is": LayerNorm(x) = gamma * (x - mean) /
+ * sqrt(variance + eps) + beta over the hidden axis.  The variance is the
+ * population variance about the row mean (divided by hidden, as in the
+ * torch LayerNorm module the page's swap loop replaces); beta may be NULL
+ * (a LayerNorm without bias). */
+void oracle_layernorm(double *y, const void *x, const void *gamma, const void *beta,
+                      int64_t rows, int64_t hidden, int64_t x_stride, double eps, int dtype)
+{
+    for (int64_t t = 0; t < rows; ++t) {
+        const int64_t row_at = t * x_stride;
+        double sum = 0.0;
+        for (int64_t i = 0; i < hidden; ++i) {
+            sum += widen(x, row_at + i, dtype);
+        }
+        double mean = sum / (double)hidden;
+        double sum_dev_sq = 0.0;
+        for (int64_t i = 0; i < hidden; ++i) {
+            double d = widen(x, row_at + i, dtype) - mean;
+            sum_dev_sq += d * d;
+        }
+        double variance = sum_dev_sq / (double)hidden;
+        double root = sqrt(variance + eps);
+        for (int64_t i = 0; i < hidden; ++i) {
+            double v = widen(gamma, i, dtype) * (widen(x, row_at + i, dtype) - mean) / root;
+            if (beta != NULL) {
+                v += widen(beta, i, dtype);
+            }
+            y[t * hidden + i] = v;
+        }
+    }
+}
+
+/* The residual add followed by LayerNorm, read like "Norm+Residual" ([P2]
+ * part 3): h = round_io(x + residual) is stored and normalised. */
+void oracle_add_layernorm(double *y, void *residual_out, const void *x,
+                          const void *residual, const void *gamma, const void *beta,
+                          int64_t rows, int64_t hidden, double eps, int dtype)
+{
+    for (int64_t t = 0; t < rows; ++t) {
+        for (int64_t i = 0; i < hidden; ++i) {
+            const int64_t at = t * hidden + i;
+            put(residual_out, at, widen(residual, at, dtype) + widen(x, at, dtype), dtype);
+        }
+    }
+    oracle_layernorm(y, residual_out, gamma, beta, rows, hidden, hidden, eps, dtype);
 }
 
 /* Which position stream drives frequency pair j: temporal, height, width. */

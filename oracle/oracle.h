@@ -27,6 +27,15 @@ void oracle_add_rmsnorm(double *y, void *residual_out, const void *x,
                         const void *residual, const void *gamma, int64_t rows,
                         int64_t hidden, double eps, int dtype);
 
+/* y[rows][hidden] (double); beta[hidden] may be NULL. */
+void oracle_layernorm(double *y, const void *x, const void *gamma, const void *beta,
+                      int64_t rows, int64_t hidden, int64_t x_stride, double eps, int dtype);
+
+/* residual_out (stored dtype) and y (double), all [rows][hidden] contiguous. */
+void oracle_add_layernorm(double *y, void *residual_out, const void *x,
+                          const void *residual, const void *gamma, const void *beta,
+                          int64_t rows, int64_t hidden, double eps, int dtype);
+
 /* q_out[tokens][n_q][D], k_out[tokens][n_kv][D] (double); pos[3][pos_stride]. */
 void oracle_mrope(double *q_out, double *k_out, const void *q, const void *k,
                   const int32_t *pos, int64_t pos_stride, int64_t tokens, int n_q_heads,

@@ -49,6 +49,17 @@ MUTANTS = [
     ("kv_cache_gets_unrotated_k", "k_cache_out[at + d] = k_rot[h * head_dim + d];",
      "k_cache_out[at + d] = widen(k, t * k_token_stride + (int64_t)h * head_dim + d, dtype);"),
     ("kv_slot_ignored", "const int64_t b = seq_idx[t], s = slot[t];", "const int64_t b = seq_idx[t], s = slot[t] > 0 ? 0 : slot[t];"),
+    ("ln_unbiased_variance", "double variance = sum_dev_sq / (double)hidden;",
+     "double variance = sum_dev_sq / (double)(hidden - 1);"),
+    ("ln_variance_not_centred", "double d = widen(x, row_at + i, dtype) - mean;",
+     "double d = widen(x, row_at + i, dtype);"),
+    ("ln_output_not_centred", "(widen(x, row_at + i, dtype) - mean) / root", "widen(x, row_at + i, dtype) / root"),
+    ("ln_eps_outside_root", "double root = sqrt(variance + eps);", "double root = sqrt(variance) + eps;"),
+    ("ln_beta_dropped", "v += widen(beta, i, dtype);", "v += 0.0;"),
+    ("ln_beta_scaled_by_gamma", "v += widen(beta, i, dtype);", "v += widen(gamma, i, dtype) * widen(beta, i, dtype);"),
+    ("ln_row_stride_ignored", "const int64_t row_at = t * x_stride;", "const int64_t row_at = t * hidden;"),
+    ("ln_add_norms_x", "oracle_layernorm(y, residual_out, gamma, beta, rows, hidden, hidden, eps, dtype);",
+     "oracle_layernorm(y, x, gamma, beta, rows, hidden, hidden, eps, dtype);"),
     ("bf16_via_fp32", "int e = ilogb(a);", "a = (double)(float)a; int e = ilogb(a);"),
 ]
 

@@ -181,6 +181,95 @@ def test_add_rmsnorm_special_cases():
     np.testing.assert_allclose(y, oracle.rmsnorm(r, gamma, 1e-6), rtol=0)
 
 
+# ----------------------------------------------------------------- layernorm
+
+def test_layernorm_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "layernorm_hand.json")))
+    y = oracle.layernorm(t32([g["x"]]), t32(g["gamma"]), t32(g["beta"]), g["eps"])[0]
+    np.testing.assert_allclose(y, g["y"], rtol=1e-15)
+
+
+@pytest.mark.parametrize("hidden", [2, 7, 256, 2048])
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.5])
+@pytest.mark.parametrize("bias", [True, False])
+def test_layernorm_matches_torch_layer_norm(hidden, eps, bias):
+    x = t32(rng.standard_normal((5, hidden)) * 3 + 1.5)
+    gamma = t32(1 + 0.1 * rng.standard_normal(hidden))
+    beta = t32(0.2 * rng.standard_normal(hidden)) if bias else None
+    eps = float(np.float32(eps))
+    want = torch.nn.functional.layer_norm(x.double(), (hidden,), gamma.double(),
+                                          None if beta is None else beta.double(), eps).numpy()
+    np.testing.assert_allclose(oracle.layernorm(x, gamma, beta, eps), want, rtol=1e-12, atol=1e-14)
+
+
+def test_layernorm_zero_mean_unit_population_variance_at_eps0():
+    # gamma = 1, no beta, eps = 0: every row comes out with mean 0 and variance 1
+    # taken over hidden (not hidden - 1) elements
+    x = t32(rng.standard_normal((9, 33)) * 4 + 7)
+    y = oracle.layernorm(x, torch.ones(33), None, 0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-14)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-14)
+
+
+def test_layernorm_two_elements_and_constant_row():
+    a, b, eps = 5.0, 2.0, 0.25
+    gamma, beta = t32([1.5, -2.0]), t32([0.125, 3.0])
+    y = oracle.layernorm(t32([[a, b]]), gamma, beta, eps)[0]
+    r = (a - b) / 2 / math.sqrt(((a - b) / 2) ** 2 + eps)
+    np.testing.assert_allclose(y, [1.5 * r + 0.125, -2.0 * -r + 3.0], rtol=1e-15)
+    beta = t32(rng.standard_normal(64))
+    y = oracle.layernorm(t32(np.full((2, 64), -3.25)), t32(rng.uniform(0.5, 2, 64)), beta, 1e-5)
+    assert np.array_equal(y, np.broadcast_to(beta.double().numpy(), (2, 64)))  # deviations are 0
+
+
+def test_layernorm_shift_and_scale_invariance():
+    # multiples of 2^-10 in [-8, 8): x + c and x * 2^k are exact in fp32
+    x = t32(np.round(rng.uniform(-8, 8, (4, 128)) * 1024) / 1024)
+    gamma, beta = t32(1 + 0.1 * rng.standard_normal(128)), t32(rng.standard_normal(128))
+    y = oracle.layernorm(x, gamma, beta, 1e-3)
+    for c in (-3.0, 0.5, 16.0):
+        np.testing.assert_allclose(oracle.layernorm(x + c, gamma, beta, 1e-3), y, rtol=1e-12, atol=1e-13)
+    for a in (2.0**-6, 4.0, 2.0**10):   # eps scales with a^2
+        np.testing.assert_allclose(oracle.layernorm(x * a, gamma, beta, 1e-3 * a * a), y, rtol=1e-12,
+                                   atol=1e-13)
+
+
+def test_layernorm_of_zero_mean_row_is_rmsnorm_plus_beta():
+    x = rng.standard_normal((3, 64))
+    x = np.concatenate([x, -x], axis=1)              # every row sums to exactly 0
+    x, gamma = t32(x), t32(1 + 0.1 * rng.standard_normal(128))
+    beta = t32(rng.standard_normal(128))
+    np.testing.assert_allclose(oracle.layernorm(x, gamma, beta, 1e-6),
+                               oracle.rmsnorm(x, gamma, 1e-6) + beta.double().numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_layernorm_row_stride_and_bf16():
+    big = tb16(rng.standard_normal((6, 96)) + 2)
+    x = big[:, 16:80]
+    gamma, beta = tb16(1 + 0.1 * rng.standard_normal(64)), tb16(rng.standard_normal(64))
+    y = oracle.layernorm(x, gamma, beta, 1e-5)
+    want = torch.nn.functional.layer_norm(x.double(), (64,), gamma.double(), beta.double(),
+                                          float(np.float32(1e-5)))
+    np.testing.assert_allclose(y, want.numpy(), rtol=1e-12, atol=1e-12)   # y ~ 1: torch rounds differently
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_add_layernorm_is_rounded_sum_then_layernorm(dt):
+    x = torch.from_numpy(rng.standard_normal((6, 256)).astype(np.float32) * 10).to(dt)
+    r = torch.from_numpy(rng.standard_normal((6, 256)).astype(np.float32)).to(dt)
+    gamma = torch.from_numpy((1 + 0.1 * rng.standard_normal(256)).astype(np.float32)).to(dt)
+    beta = torch.from_numpy(rng.standard_normal(256).astype(np.float32)).to(dt)
+    y, h = oracle.add_layernorm(x, r, gamma, beta, 1e-5)
+    assert torch.equal(h.view(torch.int16) if dt == torch.bfloat16 else h, (x + r).view(torch.int16)
+                       if dt == torch.bfloat16 else x + r)
+    want = torch.nn.functional.layer_norm((x + r).double(), (256,), gamma.double(), beta.double(),
+                                          float(np.float32(1e-5)))
+    np.testing.assert_allclose(y, want.numpy(), rtol=1e-12, atol=1e-14)
+    y0, _ = oracle.add_layernorm(x, r, gamma, None, 1e-5)
+    np.testing.assert_allclose(y - y0, np.broadcast_to(beta.double().numpy(), y.shape), rtol=1e-12,
+                               atol=1e-13)
+
+
 # ----------------------------------------------------------------- mrope
 
 def _pos(t, h, w):
