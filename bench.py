@@ -46,6 +46,10 @@ def algorithmic_bytes(op, T, H, I, nq, nkv, D, s):
         return 3 * T * I * s
     if op == "mrope_kv_append":   # q in place, k -> k cache, v -> v cache, 3 positions + seq + slot
         return 2 * (nq + 2 * nkv) * D * s * T + 20 * T
+    if op == "layernorm":         # gamma and beta
+        return 2 * T * H * s + 2 * H * s
+    if op == "add_layernorm":
+        return 4 * T * H * s + 2 * H * s
     raise ValueError(op)
 
 
@@ -309,7 +313,13 @@ def main():
     u5, u256 = torch.rand(5, device=dev), torch.rand(256, device=dev)
     tok5 = torch.empty(5, dtype=torch.int32, device=dev)
     tok256 = torch.empty(256, dtype=torch.int32, device=dev)
-    nxt = {"mrope_kv_append": (lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
+    beta = torch.empty_like(L.gamma).normal_().mul_(0.1)
+    nxt = {"layernorm": (lambda: nrs.layernorm(xn, L.gamma, beta, 1e-5, out=y),
+                         algorithmic_bytes("layernorm", T, H, I, nq, nkv, D, s)),
+           "add_layernorm": (lambda: nrs.add_layernorm(L.x, L.residual, L.gamma, beta, 1e-5, out=y2,
+                                                       residual_out=ro),
+                             algorithmic_bytes("add_layernorm", T, H, I, nq, nkv, D, s)),
+           "mrope_kv_append": (lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
                                                            kc, vc, seq0, slots),
                                algorithmic_bytes("mrope_kv_append", T, H, I, nq, nkv, D, s)),
            "softmax_topk_sample_5x3072_k50": (

@@ -94,6 +94,29 @@ int nrs_add_rmsnorm(void *y, void *residual_out, const void *x, const void *resi
                     void *stream);
 
 /*
+ * LayerNorm, [P1] section 09 "What it is":
+ *   y = gamma * (x - mean) / sqrt(variance + eps) + beta
+ * over the hidden axis of each row; variance is the population variance
+ * about the row mean (divided by hidden), as in the torch LayerNorm module
+ * the section's swap loop replaces.  Arguments as for nrs_rmsnorm, plus
+ *   beta[hidden]  in, 16-byte aligned, or NULL for a LayerNorm without bias.
+ *   y == x (exactly) is allowed.
+ */
+int nrs_layernorm(void *y, const void *x, const void *gamma, const void *beta, int64_t rows,
+                  int64_t hidden, int64_t x_stride, int64_t y_stride, float eps, int dtype,
+                  void *stream);
+
+/*
+ * Fused residual add + LayerNorm, "Norm+Residual" ([P2] part 3) with the
+ * LayerNorm of [P1] section 09:
+ *   h = round(x + residual) -> residual_out;  y = LayerNorm(h; gamma, beta, eps)
+ * Layout, limits and aliasing as for nrs_add_rmsnorm; beta may be NULL.
+ */
+int nrs_add_layernorm(void *y, void *residual_out, const void *x, const void *residual,
+                      const void *gamma, const void *beta, int64_t rows, int64_t hidden,
+                      float eps, int dtype, void *stream);
+
+/*
  * Multimodal rotary position embedding, in place on q and k.  [P3] stage 2:
  * the position enters Q and K as a rotation in the complex plane; [P2] part 3
  * names the multimodal (three-stream) variant.  For token t, every q and k

@@ -133,6 +133,27 @@ NRS_API int nrs_add_rmsnorm(void *y, void *residual_out, const void *x, const vo
                                               eps, dtype, (hipStream_t)stream));
 }
 
+NRS_API int nrs_layernorm(void *y, const void *x, const void *gamma, const void *beta,
+                          int64_t rows, int64_t hidden, int64_t x_stride, int64_t y_stride,
+                          float eps, int dtype, void *stream) {
+    int st = nrs::check_layernorm(y, x, gamma, beta, rows, hidden, x_stride, y_stride, eps, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    clear_stale_error();
+    return hip_status(nrs::launch_layernorm(y, x, gamma, beta, rows, hidden, x_stride, y_stride,
+                                            eps, dtype, (hipStream_t)stream));
+}
+
+NRS_API int nrs_add_layernorm(void *y, void *residual_out, const void *x, const void *residual,
+                              const void *gamma, const void *beta, int64_t rows, int64_t hidden,
+                              float eps, int dtype, void *stream) {
+    int st = nrs::check_add_layernorm(y, residual_out, x, residual, gamma, beta, rows, hidden, eps,
+                                      dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    clear_stale_error();
+    return hip_status(nrs::launch_add_layernorm(y, residual_out, x, residual, gamma, beta, rows,
+                                                hidden, eps, dtype, (hipStream_t)stream));
+}
+
 NRS_API int nrs_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                       int64_t q_token_stride, int64_t k_token_stride, int32_t sec_t, int32_t sec_h,

@@ -26,6 +26,12 @@ hipError_t launch_rmsnorm(void *y, const void *x, const void *gamma, int64_t row
 hipError_t launch_add_rmsnorm(void *y, void *residual_out, const void *x, const void *residual,
                               const void *gamma, int64_t rows, int64_t hidden, float eps,
                               int dtype, hipStream_t stream);
+hipError_t launch_layernorm(void *y, const void *x, const void *gamma, const void *beta,
+                            int64_t rows, int64_t hidden, int64_t x_stride, int64_t y_stride,
+                            float eps, int dtype, hipStream_t stream);
+hipError_t launch_add_layernorm(void *y, void *residual_out, const void *x, const void *residual,
+                                const void *gamma, const void *beta, int64_t rows, int64_t hidden,
+                                float eps, int dtype, hipStream_t stream);
 hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
                         int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t q_stride,
                         int64_t k_stride, int32_t sec_t, int32_t sec_h, const mrope_freqs &fr,

@@ -1,11 +1,13 @@
-// RMSNorm and fused residual-add + RMSNorm for gfx950.
+// RMSNorm, LayerNorm and their fused residual-add variants for gfx950.
 //
 // RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps), the mean over the hidden
 // axis ("Optimising autoregressive speech models", section 09 "LayerNorm ->
-// RMSNorm": "What it is" and "How to swap").  The fused variant is the
-// "Norm+Residual" op of the qwen3-tts-triton post (de.news.hada.io topic
-// 27742, part 3): h = x + residual is rounded to the storage type, written
-// as residual_out, and normalised in the same pass.
+// RMSNorm": "What it is" and "How to swap").  LayerNorm(x) = gamma * (x -
+// mean) / sqrt(variance + eps) + beta, from the same section; the variance
+// is the population variance about the row mean and beta is optional.  The
+// fused variants are the "Norm+Residual" op of the qwen3-tts-triton post
+// (de.news.hada.io topic 27742, part 3): h = x + residual is rounded to the
+// storage type, written as residual_out, and normalised in the same pass.
 //
 // Layout: a row is split over whole waves of 64 threads, each thread holding
 // NCH 16-byte chunks, so every load instruction of a wave reads 1 KiB of
@@ -19,8 +21,12 @@
 //
 // Reduction: DPP row operations plus four readlanes per wave (no LDS, no
 // barrier); rows spanning several waves add their wave sums through a few
-// bytes of LDS and one barrier.  gamma is loaded together with x (it stays
-// in L2 across rows) and applied last.
+// bytes of LDS and one barrier.  LayerNorm reduces twice within each wave,
+// the mean and then the squared deviations from it, over the registers (an
+// exact two-pass variance with no extra HBM traffic), and merges the waves'
+// moments through the same single barrier.
+// gamma and beta are loaded together with x (they stay in L2 across rows)
+// and applied last.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -29,15 +35,17 @@ namespace nrs {
 // A row is split over WPR waves of 64 threads; each thread holds NCH chunks
 // (thread t of the row owns chunks t, t + 64*WPR, ...).  Rows of one wave are
 // packed four to a block, wider rows get a block each.
-template <typename IO, int WPR, int NCH, bool ADD, bool NT>
+// LN selects LayerNorm (beta may be null) over RMSNorm.
+template <typename IO, int WPR, int NCH, bool ADD, bool LN, bool NT>
 __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
-    IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, int64_t rows,
-    int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
+    IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, const IO *beta,
+    int64_t rows, int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
     constexpr int RPB = WPR == 1 ? 4 : 1;      // rows per block
     constexpr int TPR = 64 * WPR;               // threads per row
-    __shared__ float partial[WPR * RPB];
+    __shared__ float partial[LN ? 1 : WPR * RPB];
+    __shared__ float4 moments[LN ? WPR * RPB : 1];
 
     const int wave = threadIdx.x >> 6;
     const int rib = wave / WPR;                 // row within the block
@@ -45,22 +53,26 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
     const int64_t row = (int64_t)blockIdx.x * RPB + rib;
     const bool live = row < rows;
 
-    u32x4 xr[NCH], rr[NCH], gr[NCH];
+    const bool has_beta = LN && beta != nullptr;
+    u32x4 xr[NCH], rr[NCH], gr[NCH], br[LN ? NCH : 1];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int idx = t + TPR * c;
         xr[c] = rr[c] = gr[c] = u32x4{0, 0, 0, 0};
+        if (LN) br[c] = u32x4{0, 0, 0, 0};
         if (live && idx < nchunks) {
             // gamma first: loads return in order, so waiting for x (and the
             // residual) also covers gamma, and no wait for gamma lands after the
             // residual_out store (stores count in the same vmcnt on gfx950,
             // so such a wait would stall on the store's acknowledgement)
             gr[c] = load16(gamma + (int64_t)idx * VEC);
+            if (has_beta) br[c] = load16(beta + (int64_t)idx * VEC);
             xr[c] = load16_policy<NT>(x + row * x_stride + (int64_t)idx * VEC);
             if (ADD) rr[c] = load16_policy<NT>(res + row * x_stride + (int64_t)idx * VEC);
         }
     }
 
+    // RMSNorm: ss = sum of squares.  LayerNorm: ss = sum.
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -79,15 +91,61 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
                 store16_policy<NT>(res_out + row * y_stride + (int64_t)idx * VEC, xr[c]);
         }
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+        for (int i = 0; i < VEC; ++i) ss = LN ? ss + v[i] : __builtin_fmaf(v[i], v[i], ss);
     }
     ss = wave_sum(ss);
-    if (WPR > 1) {
-        if ((threadIdx.x & 63) == 0) partial[wave] = ss;
-        __syncthreads();
-        ss = 0.0f;
+    float mean = 0.0f;
+    if (!LN) {
+        if (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) partial[wave] = ss;
+            __syncthreads();
+            ss = 0.0f;
 #pragma unroll
-        for (int w = 0; w < WPR; ++w) ss += partial[rib * WPR + w];
+            for (int w = 0; w < WPR; ++w) ss += partial[rib * WPR + w];
+        }
+    } else {
+        // LayerNorm moments with one barrier: each wave takes the exact
+        // two-pass mean and sum of squared deviations of its own elements
+        // (registers only), and the row's waves are then combined by the law of
+        // total variance, M2 = sum_w [M2_w + n_w (mean_w - mean)^2], which adds
+        // small differences only (no E[x^2] - E[x]^2 cancellation).
+        const int wir = wave - rib * WPR;       // wave within the row
+        int nw = 0;                             // elements held by this wave
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) nw += min(max(nchunks - TPR * c - 64 * wir, 0), 64);
+        nw *= VEC;
+        const float mw = nw > 0 ? ss / (float)nw : 0.0f;
+        float m2 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (t + TPR * c < nchunks) {        // lanes past the row's end add nothing
+                float v[VEC];
+                T::unpack(xr[c], v);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const float d = v[i] - mw;
+                    m2 = __builtin_fmaf(d, d, m2);
+                }
+            }
+        }
+        m2 = wave_sum(m2);
+        mean = mw;
+        if (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) moments[wave] = float4{ss, mw, m2, (float)nw};
+            __syncthreads();
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) sum += moments[rib * WPR + w].x;
+            mean = sum / (float)(nchunks * VEC);
+            m2 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                const float4 p = moments[rib * WPR + w];
+                const float d = p.y - mean;
+                m2 += __builtin_fmaf(p.w * d, d, p.z);
+            }
+        }
+        ss = m2;
     }
     if (!live) return;
     const float rs = rsqrtf(__builtin_fmaf(ss, inv_h, eps));
@@ -98,8 +156,17 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
             float v[VEC], g[VEC], o[VEC];
             T::unpack(xr[c], v);
             T::unpack(gr[c], g);
+            if (LN) {
+                float b[VEC];
+                T::unpack(br[c], b);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) o[i] = (v[i] * rs) * g[i];
+                for (int i = 0; i < VEC; ++i)
+                    o[i] = has_beta ? __builtin_fmaf((v[i] - mean) * rs, g[i], b[i])
+                                    : ((v[i] - mean) * rs) * g[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) o[i] = (v[i] * rs) * g[i];
+            }
             store16_policy<NT>(y + row * y_stride + (int64_t)idx * VEC, T::pack(o));
         }
     }
@@ -107,27 +174,32 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
 
 namespace {
 
-// Waves per row and chunks per thread: the fewest chunks per thread whose
-// wave count is 1, 2, 3, 4 or 8.  Measured at 32768 rows on MI355X, rows
-// spread over 6 or 16 waves stream 7-10% slower than the same rows over 3 or
-// 8 waves with two chunks per thread; 1-4 and 8 waves with one chunk are best.
-void norm_shape(int nchunks, int &wpr, int &nch) {
-    for (nch = 1; nch < 8; nch *= 2) {
+// Waves per row and chunks per thread: the fewest chunks per thread, from
+// min_nch up, whose wave count is 1, 2, 3, 4 or 8.  Measured at 32768 rows on
+// MI355X, RMSNorm rows spread over 6 or 16 waves stream 7-10% slower than the
+// same rows over 3 or 8 waves with two chunks per thread, and 1-4 or 8 waves
+// with one chunk are best.  LayerNorm starts from two chunks per thread: its
+// second reduction lengthens each wave's load-reduce-store chain, and with
+// one chunk per thread too few bytes stay in flight to cover it (hidden 1024
+// to 4096: 16-20% slower than with two).
+void norm_shape(int nchunks, int min_nch, int &wpr, int &nch) {
+    if (nchunks < 64 * min_nch) min_nch = 1;   // short rows: keep every lane busy
+    for (nch = min_nch; nch < 8; nch *= 2) {
         wpr = (nchunks + 64 * nch - 1) / (64 * nch);
         if (wpr <= 4 || wpr == 8) return;
     }
     wpr = (nchunks + 64 * nch - 1) / (64 * nch);
 }
 
-template <typename IO, bool ADD, int WPR, bool NT>
-void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, int64_t rows,
+template <typename IO, bool ADD, bool LN, int WPR, bool NT>
+void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, const IO *b, int64_t rows,
                   int32_t nchunks, int nch, int64_t xs, int64_t ys, float inv_h, float eps,
                   hipStream_t stream) {
     constexpr int RPB = WPR == 1 ? 4 : 1;
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(64 * WPR * RPB);
 #define NRS_NORM(N)                                                                             \
-    hipLaunchKernelGGL((norm_kernel<IO, WPR, N, ADD, NT>), grid, block, 0, stream, y, ro, x, r, g, \
-                       rows, nchunks, xs, ys, inv_h, eps)
+    hipLaunchKernelGGL((norm_kernel<IO, WPR, N, ADD, LN, NT>), grid, block, 0, stream, y, ro, x, r, \
+                       g, b, rows, nchunks, xs, ys, inv_h, eps)
     if (nch <= 1) NRS_NORM(1);
     else if (nch <= 2) NRS_NORM(2);
     else if (nch <= 4) NRS_NORM(4);
@@ -135,23 +207,24 @@ void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, int64_t 
 #undef NRS_NORM
 }
 
-template <typename IO, bool ADD>
+template <typename IO, bool ADD, bool LN>
 hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *res,
-                             const void *gamma, int64_t rows, int64_t hidden, int64_t x_stride,
-                             int64_t y_stride, float eps, hipStream_t stream) {
+                             const void *gamma, const void *beta, int64_t rows, int64_t hidden,
+                             int64_t x_stride, int64_t y_stride, float eps, hipStream_t stream) {
     constexpr int VEC = io_traits<IO>::VEC;
     const int32_t nchunks = (int32_t)(hidden / VEC);
     const float inv_h = (float)(1.0 / (double)hidden);
     int wpr, nch;
-    norm_shape(nchunks, wpr, nch);
+    norm_shape(nchunks, LN ? 2 : 1, wpr, nch);
     IO *Y = (IO *)y, *RO = (IO *)res_out;
-    const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma;
+    const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma,
+             *B = (const IO *)beta;
     const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
 #define NRS_SHAPE(W)                                                                             \
-    (nt ? launch_shape<IO, ADD, W, true>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride,  \
-                                         inv_h, eps, stream)                                      \
-        : launch_shape<IO, ADD, W, false>(Y, RO, X, R, G, rows, nchunks, nch, x_stride, y_stride, \
-                                          inv_h, eps, stream))
+    (nt ? launch_shape<IO, ADD, LN, W, true>(Y, RO, X, R, G, B, rows, nchunks, nch, x_stride,      \
+                                             y_stride, inv_h, eps, stream)                        \
+        : launch_shape<IO, ADD, LN, W, false>(Y, RO, X, R, G, B, rows, nchunks, nch, x_stride,     \
+                                              y_stride, inv_h, eps, stream))
     switch (wpr) {
         case 1: NRS_SHAPE(1); break;
         case 2: NRS_SHAPE(2); break;
@@ -170,20 +243,40 @@ hipError_t launch_rmsnorm(void *y, const void *x, const void *gamma, int64_t row
                           int64_t x_stride, int64_t y_stride, float eps, int dtype,
                           hipStream_t stream) {
     if (dtype == 0)
-        return launch_norm_typed<float, false>(y, nullptr, x, nullptr, gamma, rows, hidden,
-                                               x_stride, y_stride, eps, stream);
-    return launch_norm_typed<__bf16, false>(y, nullptr, x, nullptr, gamma, rows, hidden, x_stride,
-                                            y_stride, eps, stream);
+        return launch_norm_typed<float, false, false>(y, nullptr, x, nullptr, gamma, nullptr, rows,
+                                                      hidden, x_stride, y_stride, eps, stream);
+    return launch_norm_typed<__bf16, false, false>(y, nullptr, x, nullptr, gamma, nullptr, rows,
+                                                   hidden, x_stride, y_stride, eps, stream);
 }
 
 hipError_t launch_add_rmsnorm(void *y, void *residual_out, const void *x, const void *residual,
                               const void *gamma, int64_t rows, int64_t hidden, float eps,
                               int dtype, hipStream_t stream) {
     if (dtype == 0)
-        return launch_norm_typed<float, true>(y, residual_out, x, residual, gamma, rows, hidden,
-                                              hidden, hidden, eps, stream);
-    return launch_norm_typed<__bf16, true>(y, residual_out, x, residual, gamma, rows, hidden,
-                                           hidden, hidden, eps, stream);
+        return launch_norm_typed<float, true, false>(y, residual_out, x, residual, gamma, nullptr,
+                                                     rows, hidden, hidden, hidden, eps, stream);
+    return launch_norm_typed<__bf16, true, false>(y, residual_out, x, residual, gamma, nullptr,
+                                                  rows, hidden, hidden, hidden, eps, stream);
+}
+
+hipError_t launch_layernorm(void *y, const void *x, const void *gamma, const void *beta,
+                            int64_t rows, int64_t hidden, int64_t x_stride, int64_t y_stride,
+                            float eps, int dtype, hipStream_t stream) {
+    if (dtype == 0)
+        return launch_norm_typed<float, false, true>(y, nullptr, x, nullptr, gamma, beta, rows,
+                                                     hidden, x_stride, y_stride, eps, stream);
+    return launch_norm_typed<__bf16, false, true>(y, nullptr, x, nullptr, gamma, beta, rows,
+                                                  hidden, x_stride, y_stride, eps, stream);
+}
+
+hipError_t launch_add_layernorm(void *y, void *residual_out, const void *x, const void *residual,
+                                const void *gamma, const void *beta, int64_t rows, int64_t hidden,
+                                float eps, int dtype, hipStream_t stream) {
+    if (dtype == 0)
+        return launch_norm_typed<float, true, true>(y, residual_out, x, residual, gamma, beta,
+                                                    rows, hidden, hidden, hidden, eps, stream);
+    return launch_norm_typed<__bf16, true, true>(y, residual_out, x, residual, gamma, beta, rows,
+                                                 hidden, hidden, hidden, eps, stream);
 }
 
 }  // namespace nrs

@@ -47,6 +47,24 @@ inline int check_add_rmsnorm(const void *y, const void *residual_out, const void
     return NRS_OK;
 }
 
+inline int check_layernorm(const void *y, const void *x, const void *gamma, const void *beta,
+                           int64_t rows, int64_t hidden, int64_t x_stride, int64_t y_stride,
+                           float eps, int dtype) {
+    int st = check_rmsnorm(y, x, gamma, rows, hidden, x_stride, y_stride, eps, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    if (beta && !aligned16(beta)) return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
+inline int check_add_layernorm(const void *y, const void *residual_out, const void *x,
+                               const void *residual, const void *gamma, const void *beta,
+                               int64_t rows, int64_t hidden, float eps, int dtype) {
+    int st = check_add_rmsnorm(y, residual_out, x, residual, gamma, rows, hidden, eps, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    if (beta && !aligned16(beta)) return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
 inline int check_mrope(const void *q, const void *k, const int32_t *pos, int64_t pos_stride,
                        int64_t tokens, int32_t n_q, int32_t n_kv, int32_t head_dim,
                        int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_h,

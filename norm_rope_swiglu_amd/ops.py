@@ -28,6 +28,13 @@ def _code(t: torch.Tensor) -> int:
     raise TypeError(f"libnrs takes float32 or bfloat16 tensors, not {t.dtype}")
 
 
+def _one_dtype(*ts: torch.Tensor) -> None:
+    """The C ABI takes one dtype code per call: every float tensor must share it."""
+    if any(t.dtype != ts[0].dtype for t in ts):
+        raise TypeError("tensors of a call must share one dtype: " +
+                        ", ".join(str(t.dtype) for t in ts))
+
+
 def _dev(*ts: torch.Tensor) -> torch.device:
     d = ts[0].device
     for t in ts:
@@ -83,6 +90,7 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
     if out is None:
         out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
     y2 = _rows2d(out, "out")
+    _one_dtype(x2, gamma, y2)
     d = _dev(x2, gamma, y2)
     rows, hidden = x2.shape
     if gamma.shape != (hidden,) or not gamma.is_contiguous() or y2.shape != x2.shape:
@@ -103,6 +111,7 @@ def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, ep
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     ts = (x, residual, out, residual_out)
+    _one_dtype(*ts, gamma)
     if any(not t.is_contiguous() or t.shape != x.shape for t in ts):
         raise ValueError("x, residual, out and residual_out must be contiguous and of one shape")
     d = _dev(*ts, gamma)
@@ -114,6 +123,58 @@ def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, ep
         check(lib().nrs_add_rmsnorm(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
                                     residual.data_ptr(), gamma.data_ptr(), rows, hidden, float(eps),
                                     _code(x), _stream(d)), "nrs_add_rmsnorm")
+    return out, residual_out
+
+
+def _beta(beta, hidden):
+    if beta is not None and (beta.shape != (hidden,) or not beta.is_contiguous()):
+        raise ValueError("beta must be contiguous [hidden] or None")
+    return 0 if beta is None else beta.data_ptr()
+
+
+def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None,
+              eps: float = 1e-5, out: torch.Tensor | None = None) -> torch.Tensor:
+    """LayerNorm over the last axis; beta=None means no bias."""
+    x2 = _rows2d(x, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    y2 = _rows2d(out, "out")
+    _one_dtype(x2, gamma, y2, *(() if beta is None else (beta,)))
+    d = _dev(x2, gamma, y2, *(() if beta is None else (beta,)))
+    rows, hidden = x2.shape
+    if gamma.shape != (hidden,) or not gamma.is_contiguous() or y2.shape != x2.shape:
+        raise ValueError("gamma must be contiguous [hidden]; out must match x")
+    b = _beta(beta, hidden)
+    with _on(d):
+        check(lib().nrs_layernorm(y2.data_ptr(), x2.data_ptr(), gamma.data_ptr(), b, rows, hidden,
+                                  x2.stride(0), y2.stride(0), float(eps), _code(x2), _stream(d)),
+              "nrs_layernorm")
+    return out
+
+
+def add_layernorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                  beta: torch.Tensor | None = None, eps: float = 1e-5,
+                  out: torch.Tensor | None = None, residual_out: torch.Tensor | None = None):
+    """Returns (y, residual_out), y = LayerNorm(x + residual).  Passing out=x
+    and/or residual_out=residual updates in place."""
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    ts = (x, residual, out, residual_out)
+    _one_dtype(*ts, gamma, *(() if beta is None else (beta,)))
+    if any(not t.is_contiguous() or t.shape != x.shape for t in ts):
+        raise ValueError("x, residual, out and residual_out must be contiguous and of one shape")
+    d = _dev(*ts, gamma, *(() if beta is None else (beta,)))
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    if gamma.shape != (hidden,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be contiguous [hidden]")
+    b = _beta(beta, hidden)
+    with _on(d):
+        check(lib().nrs_add_layernorm(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+                                      residual.data_ptr(), gamma.data_ptr(), b, rows, hidden,
+                                      float(eps), _code(x), _stream(d)), "nrs_add_layernorm")
     return out, residual_out
 
 
@@ -130,6 +191,7 @@ def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: 
             raise ValueError(f"{n} heads must be packed: strides (token, {D}, 1)")
     if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
         raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    _one_dtype(q, k)
     d = _dev(q, k, pos)
     st, sh, sw = (int(s) for s in sections)
     with _on(d):
@@ -159,6 +221,7 @@ def mrope_kv_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torc
             raise ValueError(f"{n} must be contiguous int32 [tokens]")
     if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
         raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    _one_dtype(q, k, v, k_cache, v_cache)
     d = _dev(q, k, v, pos, k_cache, v_cache, seq_idx, slot)
     st, sh, sw = (int(s) for s in sections)
     with _on(d):
@@ -181,6 +244,7 @@ def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
     o2 = _rows2d(out, "out")
     if o2.shape != (rows, inter):
         raise ValueError("out must be [rows, inter]")
+    _one_dtype(gu, o2)
     d = _dev(gu, o2)
     with _on(d):
         check(lib().nrs_swiglu(o2.data_ptr(), gu.data_ptr(), rows, inter, gu.stride(0),
@@ -208,6 +272,7 @@ def softmax_topk_sample(logits: torch.Tensor, temperature: float, top_k: int, u:
     p2 = _rows2d(probs, "probs") if want else None
     if want and p2.shape != lg.shape:
         raise ValueError("probs must match logits")
+    _one_dtype(lg, *((p2,) if want else ()))
     d = _dev(lg, u, token, *((p2,) if want else ()))
     with _on(d):
         check(lib().nrs_softmax_topk_sample(

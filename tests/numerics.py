@@ -9,6 +9,12 @@ bf16 outputs: distance in representable steps between the kernel's bf16 and
 the oracle value rounded to bf16 (nearest, ties to even).  Bit patterns are
 mapped to monotone integers with +0 and -0 both at 0, so the step distance is
 defined across binade edges and zero.
+
+LayerNorm outputs are measured against the size of the terms that make each
+element rather than the element itself: gamma * (x - mean) / sigma cancels to
+~0 near the mean (and against beta), while an fp32 evaluation carries the
+mean's own rounding, ~u * mean|x|, into every deviation.  ln_scale gives
+|gamma| * (|x - mean| + mean|x|) / sigma + |beta| per element.
 """
 from __future__ import annotations
 
@@ -52,6 +58,14 @@ def pair_norm(r: np.ndarray) -> np.ndarray:
     half = r.shape[-1] // 2
     n = np.hypot(r[..., :half], r[..., half:])
     return np.concatenate([n, n], axis=-1)
+
+
+def ln_scale(h: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndarray:
+    """Per-element magnitude of LayerNorm's terms for rows h [rows, hidden] (fp64)."""
+    mean = h.mean(axis=1, keepdims=True)
+    sigma = np.sqrt(((h - mean) ** 2).mean(axis=1, keepdims=True) + eps)
+    s = np.abs(gamma) * (np.abs(h - mean) + np.abs(h).mean(axis=1, keepdims=True)) / sigma
+    return s if beta is None else s + np.abs(beta)
 
 
 def cosine(a: np.ndarray, b: np.ndarray) -> float:

@@ -9,6 +9,9 @@ Pass bars:
     rotation cancels it far below its pair's norm: there any fp32 evaluation
     carries an absolute error of a few 2^-24 of the pair norm, so the bar is
     |y - r| <= 2^-20 * |pair|; such elements are counted.
+  LayerNorm: as above with the error measured against ln_scale (the size of
+    the terms that make the element) in place of the element's own value; a
+    bf16 element may exceed 1 step only within 2^-20 of that scale (counted).
   residual_out: bit-exact.
 Cosine similarity is recorded for every compared tensor.
 """
@@ -21,20 +24,23 @@ import numpy as np
 import torch
 
 import oracle
-from numerics import bf16_steps, cosine, pair_norm, pair_rel_err, rel_err
+from numerics import FLT_MIN, bf16_steps, cosine, pair_norm, pair_rel_err, rel_err
 
 F32_TOL = 1e-5
 PAIR_ABS = 2.0**-20
 REPORT = []
 
 
-def check(name: str, y: torch.Tensor, r: np.ndarray, pairs: bool = False) -> dict:
+def check(name: str, y: torch.Tensor, r: np.ndarray, pairs: bool = False, scale=None) -> dict:
     y = y.detach().cpu()
     yd = y.double().numpy().reshape(r.shape)
     rec = {"name": name, "dtype": str(y.dtype).replace("torch.", ""), "n": int(r.size),
            "cosine": cosine(yd, r)}
     if y.dtype == torch.float32:
-        err = pair_rel_err(yd, r) if pairs else rel_err(yd, r)
+        if scale is not None:
+            err = np.abs(yd - r) / np.maximum(scale, FLT_MIN)
+        else:
+            err = pair_rel_err(yd, r) if pairs else rel_err(yd, r)
         worst = float(err.max()) if err.size else 0.0
         rec["max_rel_err"] = worst
         REPORT.append(rec)
@@ -47,8 +53,8 @@ def check(name: str, y: torch.Tensor, r: np.ndarray, pairs: bool = False) -> dic
     steps = bf16_steps(y, ref).reshape(r.shape)
     bad = steps > 1
     n_cancel = 0
-    if pairs:
-        ok_abs = np.abs(yd - r) <= PAIR_ABS * pair_norm(r)
+    if pairs or scale is not None:
+        ok_abs = np.abs(yd - r) <= PAIR_ABS * (pair_norm(r) if pairs else scale)
         n_cancel = int((bad & ok_abs).sum())
         bad &= ~ok_abs
     rec.update(max_steps=int(steps.max()) if steps.size else 0,

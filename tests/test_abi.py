@@ -104,6 +104,50 @@ def test_add_rmsnorm_rejects(L, args, want):
     assert L.nrs_add_rmsnorm(*args, None) == want
 
 
+LN = [  # (y, x, gamma, beta, rows, hidden, x_stride, y_stride, eps, dtype)
+    ((P, P, P, P, 4, 256, 256, 256, 1e-5, 2), DTYPE),
+    ((P, P, P, P, 4, 100, 100, 100, 1e-5, 1), SHAPE),
+    ((P, P, P, P, 4, 256, 128, 256, 1e-5, 1), SHAPE),
+    ((P, P, P, P, 4, 256, 256, 256, -1.0, 1), ARG),
+    ((P, P, None, P, 4, 256, 256, 256, 1e-5, 1), NULL),
+    ((P, P, P, U, 4, 256, 256, 256, 1e-5, 1), ALIGN),     # beta misaligned
+    ((P, U, P, None, 4, 256, 256, 256, 1e-5, 1), ALIGN),  # no beta, x misaligned
+    ((None, None, None, None, 0, 256, 256, 256, 1e-5, 1), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", LN)
+def test_layernorm_rejects(L, args, want):
+    assert L.nrs_layernorm(*args, None) == want
+
+
+ADD_LN = [  # (y, residual_out, x, residual, gamma, beta, rows, hidden, eps, dtype)
+    ((P, None, P, P, P, P, 4, 256, 1e-5, 1), NULL),
+    ((P, P, P, P, P, U, 4, 256, 1e-5, 1), ALIGN),
+    ((P, P, P, U, P, None, 4, 256, 1e-5, 1), ALIGN),
+    ((P, P, P, P, P, P, 4, 12, 1e-5, 1), SHAPE),
+    ((P, P, P, P, P, P, 4, 256, float("nan"), 0), ARG),
+    ((P, P, P, P, P, P, 4, 256, 1e-5, 7), DTYPE),
+    ((None, None, None, None, None, None, 0, 256, 1e-5, 0), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", ADD_LN)
+def test_add_layernorm_rejects(L, args, want):
+    assert L.nrs_add_layernorm(*args, None) == want
+
+
+def test_binding_rejects_mixed_dtypes():
+    import torch
+    import norm_rope_swiglu_amd as nrs
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.float32)
+    for call in (lambda: nrs.rmsnorm(x, g), lambda: nrs.layernorm(x, g.bfloat16(), g),
+                 lambda: nrs.add_rmsnorm(x, x, g), lambda: nrs.add_layernorm(x, x.float(), g)):
+        with pytest.raises(TypeError):
+            call()
+
+
 def mr(q=P, k=P, pos=P, pos_stride=8, tokens=8, nq=4, nkv=2, D=64, qs=256, ks=128,
        sec=(8, 12, 12), theta=1e6, dtype=1):
     return (q, k, pos, pos_stride, tokens, nq, nkv, D, qs, ks, *sec, theta, dtype)

@@ -1,6 +1,6 @@
 """GPU parity of the ops beyond the four-op hot path, through the C ABI,
-against the fp64 oracle: M-RoPE fused with the KV-cache append, and fused
-softmax + top-k sampling."""
+against the fp64 oracle: M-RoPE fused with the KV-cache append, fused
+softmax + top-k sampling, and LayerNorm with its fused residual add."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,6 +10,7 @@ import torch
 import norm_rope_swiglu_amd as nrs
 import oracle
 import workloads as W
+from numerics import ln_scale
 from parity import check, check_exact
 
 pytestmark = pytest.mark.gpu
@@ -200,3 +201,125 @@ def test_sample_inverse_cdf_frequencies():
     _, probs, _, _ = oracle.softmax_topk_sample(lg[:1], 1.0, 64, np.zeros(1, np.float32))
     counts = np.bincount(tok, minlength=64)
     assert np.all(np.abs(counts - N * probs[0]) <= 2.0)
+
+
+# ------------------------------------------------------------ LayerNorm
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+def _ln_inputs(rows, hidden, dt, seed=0, offset=3.0, bias=True):
+    """Rows with their own mean and spread (LayerNorm's inputs are not
+    centred), gamma ~ 1 + 0.1 N, beta ~ 0.1 N."""
+    def key(n):
+        return W.stream_key(seed, f"ln/{n}/{rows}/{hidden}/{offset}")
+    mu = W.normal(key("mu"), rows).reshape(rows, 1) * offset
+    sd = torch.exp(W.normal(key("sd"), rows).reshape(rows, 1) * 0.5)
+    x = W.normal(key("x"), rows * hidden).reshape(rows, hidden) * sd + mu
+    gamma = 1 + 0.1 * W.normal(key("g"), hidden)
+    beta = 0.1 * W.normal(key("b"), hidden) if bias else None
+    return W.store(x, dt), W.store(gamma, dt), None if beta is None else W.store(beta, dt)
+
+
+def ln_parity(x, gamma, beta, eps, tag, residual=None, rows=None):
+    """nrs.layernorm / nrs.add_layernorm against the oracle, on every row or
+    on the sampled `rows` of a full-size launch."""
+    cu = (lambda t: None if t is None else t.cuda())
+    if residual is None:
+        y = nrs.layernorm(cu(x), cu(gamma), cu(beta), eps).cpu()
+        ro = None
+    else:
+        y, ro = nrs.add_layernorm(cu(x), cu(residual), cu(gamma), cu(beta), eps)
+        y, ro = y.cpu(), ro.cpu()
+    sel = slice(None) if rows is None else rows
+    xs = x[sel].contiguous()
+    if residual is None:
+        ry, h = oracle.layernorm(xs, gamma, beta, _f32(eps)), xs
+    else:
+        ry, h = oracle.add_layernorm(xs, residual[sel].contiguous(), gamma, beta, _f32(eps))
+        check_exact(f"{tag}/residual_out", ro[sel], h)
+    sc = ln_scale(oracle.widen(h).reshape(h.shape), oracle.widen(gamma),
+                  None if beta is None else oracle.widen(beta), _f32(eps))
+    check(f"{tag}/y", y[sel], ry, scale=sc)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("hidden", [8, 24, 200, 1024, 1280, 1600, 2048, 5120, 8192, 12288, 32768])
+def test_layernorm_widths(dt, hidden):
+    if dt == "f32" and hidden in (8, 24):
+        hidden //= 2                               # fp32 rows need multiples of 4 only
+    rows = 37 if hidden <= 8192 else 5
+    bias = hidden % 3 != 1
+    x, g, b = _ln_inputs(rows, hidden, dt, 1, bias=bias)
+    ln_parity(x, g, b, 1e-5, f"ln/{dt}/H{hidden}")
+    r, _, _ = _ln_inputs(rows, hidden, dt, 2, offset=1.0)
+    ln_parity(x, g, b, 1e-5, f"add_ln/{dt}/H{hidden}", residual=r)
+
+
+def test_layernorm_widest_rows():
+    x, g, b = _ln_inputs(3, 65536, "bf16", 3)
+    ln_parity(x, g, b, 1e-5, "ln/bf16/H65536")
+    ln_parity(x, g, b, 1e-5, "add_ln/bf16/H65536", residual=x.flip(0).contiguous())
+
+
+@pytest.mark.parametrize("rows", [1, 3, 4, 5, 255, 257])
+def test_layernorm_row_counts(rows):
+    x, g, b = _ln_inputs(rows, 1024, "bf16", 4)
+    ln_parity(x, g, b, 1e-6, f"ln/rows{rows}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_layernorm_cancellation_and_degenerate_rows(dt):
+    # far-off means (|mean| / sigma ~ 1e3), constant rows (variance 0: y = beta
+    # up to the mean's rounding), eps dominating a tiny variance
+    x, g, b = _ln_inputs(16, 2048, dt, 5, offset=1000.0)
+    ln_parity(x, g, b, 1e-5, f"ln/{dt}/offset")
+    c = torch.full((4, 2048), 0.0)
+    c[0] = 3.0
+    c[1] = -0.15625
+    c[2] = 7.1
+    c[3, ::2], c[3, 1::2] = 1e-4, -1e-4
+    ln_parity(W.store(c, dt), g, b, 1e-5, f"ln/{dt}/degenerate")
+    y = nrs.layernorm(W.store(c, dt)[:2].cuda(), g.cuda(), b.cuda(), 1e-5).cpu()
+    assert torch.equal(y, b.expand(2, -1))        # sums and means of c[0], c[1] are exact
+
+
+def test_layernorm_strided_in_place_and_empty():
+    big, g, b = _ln_inputs(9, 3072, "bf16", 6)
+    xd = big.cuda()[:, 512:2560]                  # rows of stride 3072
+    y = nrs.layernorm(xd, g[:2048].contiguous().cuda(), b[:2048].contiguous().cuda(), 1e-5)
+    ry = oracle.layernorm(big[:, 512:2560], g[:2048].contiguous(), b[:2048].contiguous(), _f32(1e-5))
+    check("ln/strided", y, ry, scale=ln_scale(oracle.widen(big[:, 512:2560].contiguous()).reshape(9, 2048),
+                                               oracle.widen(g[:2048].contiguous()),
+                                               oracle.widen(b[:2048].contiguous()), _f32(1e-5)))
+    z = big[:, 512:2560].contiguous().cuda()     # the same rows, in place
+    nrs.layernorm(z, g[:2048].contiguous().cuda(), b[:2048].contiguous().cuda(), 1e-5, out=z)
+    check_exact("ln/in_place", z, y.cpu())
+    e = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    gg = torch.ones(256, dtype=torch.bfloat16, device="cuda")
+    assert nrs.layernorm(e, gg).shape == (0, 256)
+    yy, rr = nrs.add_layernorm(e, e.clone(), gg, gg)
+    assert yy.shape == rr.shape == (0, 256)
+
+
+def test_add_layernorm_in_place():
+    x, g, b = _ln_inputs(64, 1024, "bf16", 7)
+    r, _, _ = _ln_inputs(64, 1024, "bf16", 8)
+    y, ro = nrs.add_layernorm(x.cuda(), r.cuda(), g.cuda(), b.cuda(), 1e-5)
+    xd, rd = x.cuda(), r.cuda()
+    nrs.add_layernorm(xd, rd, g.cuda(), b.cuda(), 1e-5, out=xd, residual_out=rd)
+    check_exact("add_ln/in_place.y", xd, y.cpu())
+    check_exact("add_ln/in_place.residual_out", rd, ro.cpu())
+
+
+@pytest.mark.parametrize("add", [False, True])
+def test_layernorm_full_size_sampled(add):
+    # the benchmark's launch: 32768 rows x 2048, bf16, streaming stores
+    T, H = 32768, 2048
+    x, g, b = _ln_inputs(T, H, "bf16", 9)
+    r = _ln_inputs(T, H, "bf16", 10, offset=1.0)[0] if add else None
+    gen = torch.Generator().manual_seed(11)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, 2, 3, T - 2, T - 1]),
+                                   torch.randint(0, T, (58,), generator=gen)]))
+    ln_parity(x, g, b, 1e-5, f"{'add_' if add else ''}ln/32k", residual=r, rows=rows)
