@@ -36,6 +36,7 @@ def lib():
         L.oracle_add_rmsnorm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _dbl, _int]
         L.oracle_layernorm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _dbl, _int]
         L.oracle_add_layernorm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _dbl, _int]
+        L.oracle_rmsnorm_linear.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _int]
         L.oracle_mrope.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int,
                                    _i64, _i64, _int, _int, _int, _dbl, _int]
         L.oracle_swiglu.argtypes = [_vp, _vp, _i64, _i64, _i64, _int]
@@ -46,7 +47,8 @@ def lib():
                                              _vp, _vp, _i64, _i64, _int]
         for f in ("oracle_round", "oracle_widen", "oracle_rmsnorm", "oracle_add_rmsnorm",
                   "oracle_mrope", "oracle_swiglu", "oracle_mrope_kv_append",
-                  "oracle_softmax_topk_sample", "oracle_layernorm", "oracle_add_layernorm"):
+                  "oracle_softmax_topk_sample", "oracle_layernorm", "oracle_add_layernorm",
+                  "oracle_rmsnorm_linear"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -136,6 +138,18 @@ def add_layernorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, 
     lib().oracle_add_layernorm(_ptr(y), _ptr(res_out), _ptr(x), _ptr(residual), _ptr(g),
                                None if b is None else _ptr(b), rows, hidden, float(eps), _code(x))
     return y, res_out
+
+
+def rmsnorm_linear(x: torch.Tensor, w: torch.Tensor, eps: float) -> np.ndarray:
+    """x: [rows, n_in], w: [n_out, n_in] (unit column strides; rows may be strided)."""
+    x, w = _cpu(x), _cpu(w)
+    assert x.dim() == 2 and w.dim() == 2 and x.stride(1) == 1 and w.stride(1) == 1
+    assert x.dtype == w.dtype and x.shape[1] == w.shape[1]
+    rows, n_in = x.shape
+    out = np.empty((rows, w.shape[0]), dtype=np.float64)
+    lib().oracle_rmsnorm_linear(_ptr(out), _ptr(x), _ptr(w), rows, n_in, w.shape[0], x.stride(0),
+                                w.stride(0), float(eps), _code(x))
+    return out
 
 
 def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: float):

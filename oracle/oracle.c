@@ -26,6 +26,7 @@
  *     the norm sees that rounded h.
  *   - LayerNorm: population variance about the row mean; beta optional; the
  *     fused add variant stores and normalises the rounded h as above.
+ *   - RMSNorm + Linear: no gain; weight [n_out][n_in] (torch's Linear layout).
  *   - M-RoPE: half-split pairs (j, j + D/2); pairs [0, s_t) follow the
  *     temporal stream, [s_t, s_t+s_h) the height stream, the rest the width
  *     stream; frequency theta^(-2j/D) as in standard RoPE, same for all
@@ -195,6 +196,39 @@ void oracle_add_layernorm(double *y, void *residual_out, const void *x,
         }
     }
     oracle_layernorm(y, residual_out, gamma, beta, rows, hidden, hidden, eps, dtype);
+}
+
+/* [P1] "Custom Triton kernels", kernel 1 (fused RMSNorm + Linear): each row
+ * is divided by its root-mean-square sqrt(mean(x^2) + eps), written in the
+ * listing's sqrt-then-divide form, and multiplied by the weight; no gain is
+ * applied (a gain folds into the weight's columns).  The weight is stored as
+ * torch's Linear stores it, [n_out][n_in]:
+ *   out[m][k] = sum_n (x[m][n] / rms_m) * w[k][n]. */
+void oracle_rmsnorm_linear(double *out, const void *x, const void *w, int64_t rows,
+                           int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
+                           double eps, int dtype)
+{
+    double *xn = malloc((size_t)(n_in > 0 ? n_in : 1) * sizeof *xn);
+    for (int64_t m = 0; m < rows; ++m) {
+        const int64_t xrow = m * x_stride;
+        double sum_sq = 0.0;
+        for (int64_t n = 0; n < n_in; ++n) {
+            double v = widen(x, xrow + n, dtype);
+            sum_sq += v * v;
+        }
+        double rms = sqrt(sum_sq / (double)n_in + eps);
+        for (int64_t n = 0; n < n_in; ++n) {
+            xn[n] = widen(x, xrow + n, dtype) / rms;
+        }
+        for (int64_t k = 0; k < n_out; ++k) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < n_in; ++n) {
+                acc += xn[n] * widen(w, k * w_stride + n, dtype);
+            }
+            out[m * n_out + k] = acc;
+        }
+    }
+    free(xn);
 }
 
 /* Which position stream drives frequency pair j: temporal, height, width. */

@@ -36,6 +36,12 @@ void oracle_add_layernorm(double *y, void *residual_out, const void *x,
                           const void *residual, const void *gamma, const void *beta,
                           int64_t rows, int64_t hidden, double eps, int dtype);
 
+/* out[rows][n_out] (double) from x rows of stride x_stride and w[n_out] rows
+ * of stride w_stride (each n_in long). */
+void oracle_rmsnorm_linear(double *out, const void *x, const void *w, int64_t rows,
+                           int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
+                           double eps, int dtype);
+
 /* q_out[tokens][n_q][D], k_out[tokens][n_kv][D] (double); pos[3][pos_stride]. */
 void oracle_mrope(double *q_out, double *k_out, const void *q, const void *k,
                   const int32_t *pos, int64_t pos_stride, int64_t tokens, int n_q_heads,

@@ -60,6 +60,12 @@ MUTANTS = [
     ("ln_row_stride_ignored", "const int64_t row_at = t * x_stride;", "const int64_t row_at = t * hidden;"),
     ("ln_add_norms_x", "oracle_layernorm(y, residual_out, gamma, beta, rows, hidden, hidden, eps, dtype);",
      "oracle_layernorm(y, x, gamma, beta, rows, hidden, hidden, eps, dtype);"),
+    ("lin_no_rms", "xn[n] = widen(x, xrow + n, dtype) / rms;", "xn[n] = widen(x, xrow + n, dtype);"),
+    ("lin_rms_sum_not_mean", "double rms = sqrt(sum_sq / (double)n_in + eps);", "double rms = sqrt(sum_sq + eps);"),
+    ("lin_eps_outside_root", "double rms = sqrt(sum_sq / (double)n_in + eps);", "double rms = sqrt(sum_sq / (double)n_in) + eps;"),
+    ("lin_w_stride_ignored", "widen(w, k * w_stride + n, dtype)", "widen(w, k * n_in + n, dtype)"),
+    ("lin_x_stride_ignored", "const int64_t xrow = m * x_stride;", "const int64_t xrow = m * n_in;"),
+    ("lin_w_row_off_by_one", "widen(w, k * w_stride + n, dtype)", "widen(w, (k > 0 ? k - 1 : k) * w_stride + n, dtype)"),
     ("bf16_via_fp32", "int e = ilogb(a);", "a = (double)(float)a; int e = ilogb(a);"),
 ]
 

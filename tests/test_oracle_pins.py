@@ -270,6 +270,56 @@ def test_add_layernorm_is_rounded_sum_then_layernorm(dt):
                                atol=1e-13)
 
 
+# ----------------------------------------------------------------- rmsnorm + linear
+
+def test_rmsnorm_linear_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "rmsnorm_linear_hand.json")))
+    out = oracle.rmsnorm_linear(t32(g["x"]), t32(g["w"]), g["eps"])
+    np.testing.assert_allclose(out, g["out"], rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("n_in,n_out", [(8, 3), (64, 200), (256, 96)])
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.25])
+def test_rmsnorm_linear_is_rmsnorm_then_matmul(n_in, n_out, eps):
+    # the pinned RMSNorm (gain 1) followed by numpy's matmul with w transposed
+    x = t32(rng.standard_normal((7, n_in)) * 2)
+    w = t32(rng.standard_normal((n_out, n_in)) / math.sqrt(n_in))
+    eps = float(np.float32(eps))
+    want = oracle.rmsnorm(x, torch.ones(n_in), eps) @ w.double().numpy().T
+    np.testing.assert_allclose(oracle.rmsnorm_linear(x, w, eps), want, rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_linear_gain_folds_into_weight_columns():
+    x = t32(rng.standard_normal((4, 48)))
+    gamma = t32(1 + 0.2 * rng.standard_normal(48))
+    w = t32(rng.standard_normal((20, 48)))
+    folded = t32(w.double().numpy() * gamma.double().numpy()[None, :])
+    want = oracle.rmsnorm(x, gamma, 1e-6) @ w.double().numpy().T
+    np.testing.assert_allclose(oracle.rmsnorm_linear(x, folded, 1e-6), want, rtol=1e-6, atol=1e-6)
+
+
+def test_rmsnorm_linear_identity_weight_and_invariances():
+    x = t32(rng.standard_normal((5, 32)))
+    eye = torch.eye(32)
+    np.testing.assert_allclose(oracle.rmsnorm_linear(x, eye, 1e-6),
+                               oracle.rmsnorm(x, torch.ones(32), 1e-6), rtol=1e-14, atol=0)
+    w = t32(rng.standard_normal((9, 32)))
+    base = oracle.rmsnorm_linear(x, w, 0.0)
+    for a in (2.0**-5, 8.0):                         # scale-free at eps = 0
+        np.testing.assert_allclose(oracle.rmsnorm_linear(x * a, w, 0.0), base, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oracle.rmsnorm_linear(x, w * 4, 0.0), 4 * base, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(oracle.rmsnorm_linear(x, w[[3, 0, 8]], 0.0), base[:, [3, 0, 8]], rtol=0)
+
+
+def test_rmsnorm_linear_strides_and_bf16():
+    xb = tb16(rng.standard_normal((6, 100)))
+    wb = tb16(rng.standard_normal((40, 90)) * 0.1)
+    x, w = xb[:, 10:74], wb[3:37, 20:84]             # strided rows of both operands
+    out = oracle.rmsnorm_linear(x, w, 1e-5)
+    want = torch.nn.functional.rms_norm(x.double(), (64,), None, float(np.float32(1e-5))) @ w.double().T
+    np.testing.assert_allclose(out, want.numpy(), rtol=1e-11, atol=1e-12)
+
+
 # ----------------------------------------------------------------- mrope
 
 def _pos(t, h, w):
