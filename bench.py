@@ -327,6 +327,40 @@ def main():
            "softmax_topk_sample_256x151936_k50": (
                lambda: nrs.softmax_topk_sample(lg_big, 1.0, 50, u256, token=tok256),
                256 * 151936 * 2 + 256 * 8)}
+    # fused RMSNorm + Linear at the decode step's projection shapes: 5 rows of 2048 into
+    # qkv (4096) and gate_up (12288), one distinct weight per layer for 28 layers (so each
+    # call streams its weight from HBM, 0.5-1.4 GB in all); recorded in a graph, so the
+    # time per call has no host launch cost in it
+    lin_x = torch.empty(5, H, device=dev).normal_().to(torch.bfloat16)
+    lin = {}
+    for n_out in (4096, 12288):
+        ws = [torch.empty(n_out, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
+              for _ in range(28)]
+        yo = torch.empty(5, n_out, dtype=torch.bfloat16, device=dev)
+        gs = torch.cuda.Stream(dev)
+        with torch.cuda.stream(gs):
+            for wt in ws:
+                nrs.rmsnorm_linear(lin_x, wt, 1e-6, out=yo)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for wt in ws:
+                nrs.rmsnorm_linear(lin_x, wt, 1e-6, out=yo)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / (K * 28)
+        byts = n_out * H * 2 + 5 * H * 2 + 5 * n_out * 2
+        lin[f"rmsnorm_linear_5x2048x{n_out}_graph28"] = {
+            "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del ws, graph
     for op, (fn, byts) in nxt.items():
         for _ in range(3):
             fn()
@@ -343,6 +377,7 @@ def main():
         next_ops[op] = {"mean_us": round(mean_us, 2), "bytes": byts,
                         "GB_s": round(byts / (mean_us * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(byts / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    next_ops.update(lin)
     del v, kc, vc, lg_dec, lg_big
     print(f"bench: next {json.dumps(next_ops)}", file=sys.stderr, flush=True)
 

@@ -117,6 +117,25 @@ int nrs_add_layernorm(void *y, void *residual_out, const void *x, const void *re
                       float eps, int dtype, void *stream);
 
 /*
+ * Fused RMSNorm + Linear, [P1] "Custom Triton kernels", kernel 1: each row
+ * is normalised by its root-mean-square and multiplied by the weight in one
+ * kernel, with no gain (a gain folds into the weight's columns):
+ *   out[m][k] = sum_n (x[m][n] / rms_m) * w[k][n],  rms_m = sqrt(mean_n x[m][n]^2 + eps)
+ *   x[rows][x_stride]  in; w[out_features][w_stride]  in (torch's Linear
+ *   layout, input index fastest); out[rows][out_stride]  out.
+ *   in_features: a multiple of 8 (bf16) or 4 (fp32), at most 2^20;
+ *   1 <= out_features < 2^31; strides >= the row widths; eps >= 0, finite.
+ *   x and w follow the 16-byte rules above; out needs only element alignment
+ *   and any out_stride (it is written element by element).
+ * Products are accumulated in fp32 on the matrix cores and each row is scaled
+ * by 1/rms at the end; the normalised row is never stored.  out must not
+ * overlap x or w.
+ */
+int nrs_rmsnorm_linear(void *out, const void *x, const void *w, int64_t rows, int64_t in_features,
+                       int64_t out_features, int64_t x_stride, int64_t w_stride,
+                       int64_t out_stride, float eps, int dtype, void *stream);
+
+/*
  * Multimodal rotary position embedding, in place on q and k.  [P3] stage 2:
  * the position enters Q and K as a rotation in the complex plane; [P2] part 3
  * names the multimodal (three-stream) variant.  For token t, every q and k

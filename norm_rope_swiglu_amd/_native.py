@@ -48,6 +48,7 @@ SIGNATURES = {
     "nrs_last_hip_error": (_int, []),
     "nrs_rmsnorm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp]),
     "nrs_add_rmsnorm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]),
+    "nrs_rmsnorm_linear": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]),
     "nrs_layernorm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp]),
     "nrs_add_layernorm": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]),
     "nrs_mrope": (_int, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64,

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnrs.so")
-SOURCES = ["norm.hip", "mrope.hip", "swiglu.hip", "sample.hip", "api.hip"]
+SOURCES = ["norm.hip", "mrope.hip", "swiglu.hip", "sample.hip", "linear.hip", "api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

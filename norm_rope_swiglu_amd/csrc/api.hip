@@ -154,6 +154,19 @@ NRS_API int nrs_add_layernorm(void *y, void *residual_out, const void *x, const 
                                                 hidden, eps, dtype, (hipStream_t)stream));
 }
 
+NRS_API int nrs_rmsnorm_linear(void *out, const void *x, const void *w, int64_t rows,
+                               int64_t in_features, int64_t out_features, int64_t x_stride,
+                               int64_t w_stride, int64_t out_stride, float eps, int dtype,
+                               void *stream) {
+    int st = nrs::check_rmsnorm_linear(out, x, w, rows, in_features, out_features, x_stride,
+                                       w_stride, out_stride, eps, dtype);
+    if (st != NRS_OK || rows == 0) return st;
+    clear_stale_error();
+    return hip_status(nrs::launch_rmsnorm_linear(out, x, w, rows, in_features, out_features,
+                                                 x_stride, w_stride, out_stride, eps, dtype,
+                                                 (hipStream_t)stream));
+}
+
 NRS_API int nrs_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                       int64_t q_token_stride, int64_t k_token_stride, int32_t sec_t, int32_t sec_h,

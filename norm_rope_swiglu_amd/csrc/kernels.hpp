@@ -48,6 +48,9 @@ hipError_t launch_topk_sample(int32_t *token, void *probs, const void *logits, i
                               int64_t vocab, int64_t row_stride, int64_t probs_stride,
                               float temperature, int32_t top_k, const float *u, int dtype,
                               hipStream_t stream);
+hipError_t launch_rmsnorm_linear(void *out, const void *x, const void *w, int64_t rows,
+                                 int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
+                                 int64_t out_stride, float eps, int dtype, hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);
 
 }  // namespace nrs

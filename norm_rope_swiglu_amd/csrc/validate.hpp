@@ -126,6 +126,27 @@ inline int check_swiglu(const void *out, const void *gate_up, int64_t rows, int6
     return NRS_OK;
 }
 
+constexpr int64_t kMaxLinearIn = 1 << 20;
+constexpr int64_t kMaxLinearOut = (int64_t)1 << 31;
+
+inline int check_rmsnorm_linear(const void *out, const void *x, const void *w, int64_t rows,
+                                int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
+                                int64_t out_stride, float eps, int dtype) {
+    if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
+    if (rows < 0 || n_in <= 0 || n_in % vec_of(dtype) != 0 || n_in > kMaxLinearIn || n_out <= 0 ||
+        n_out >= kMaxLinearOut)
+        return NRS_ERR_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return NRS_ERR_ARG;
+    if (rows == 0) return NRS_OK;
+    if (x_stride < n_in || w_stride < n_in || out_stride < n_out) return NRS_ERR_SHAPE;
+    if (!out || !x || !w) return NRS_ERR_NULL;
+    // out is written element by element: element alignment and any stride suffice
+    if (((uintptr_t)out & (uintptr_t)(elem_size(dtype) - 1)) != 0 || !aligned16(x) ||
+        !aligned16(w) || !stride_ok(x_stride, dtype) || !stride_ok(w_stride, dtype))
+        return NRS_ERR_ALIGN;
+    return NRS_OK;
+}
+
 constexpr int kMaxTopK = 1024;
 
 inline int check_topk_sample(const int32_t *token, const void *probs, const void *logits,

@@ -178,6 +178,31 @@ def add_layernorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
     return out, residual_out
 
 
+def rmsnorm_linear(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """(x / rms(x)) @ w.T over the last axis of x, with w [out_features,
+    in_features] (torch's Linear layout; fold any RMSNorm gain into w)."""
+    x2 = _rows2d(x, "x")
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be [out_features, in_features] with unit inner stride")
+    rows, n_in = x2.shape
+    n_out = w.shape[0]
+    if w.shape[1] != n_in:
+        raise ValueError("w's in_features must match x's last dimension")
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (n_out,), dtype=x.dtype, device=x.device)
+    o2 = _rows2d(out, "out")
+    if o2.shape != (rows, n_out):
+        raise ValueError("out must be [rows, out_features]")
+    _one_dtype(x2, w, o2)
+    d = _dev(x2, w, o2)
+    with _on(d):
+        check(lib().nrs_rmsnorm_linear(o2.data_ptr(), x2.data_ptr(), w.data_ptr(), rows, n_in, n_out,
+                                       x2.stride(0), w.stride(0), o2.stride(0), float(eps),
+                                       _code(x2), _stream(d)), "nrs_rmsnorm_linear")
+    return out
+
+
 def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: float = 1e6):
     """In place.  q: [T, n_q, D], k: [T, n_kv, D] with packed heads (token
     strides free); pos: int32 [3, >=T] with unit inner stride."""

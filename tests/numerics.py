@@ -15,6 +15,11 @@ element rather than the element itself: gamma * (x - mean) / sigma cancels to
 ~0 near the mean (and against beta), while an fp32 evaluation carries the
 mean's own rounding, ~u * mean|x|, into every deviation.  ln_scale gives
 |gamma| * (|x - mean| + mean|x|) / sigma + |beta| per element.
+
+RMSNorm + Linear outputs are dot products accumulated in fp32: their error is
+bounded by the number of roundings along the longest addition chain times
+u = 2^-24 times sum_n |x_n / rms * w_kn| (dot_scale), whatever the output's
+own size after cancellation.
 """
 from __future__ import annotations
 
@@ -66,6 +71,12 @@ def ln_scale(h: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndarray:
     sigma = np.sqrt(((h - mean) ** 2).mean(axis=1, keepdims=True) + eps)
     s = np.abs(gamma) * (np.abs(h - mean) + np.abs(h).mean(axis=1, keepdims=True)) / sigma
     return s if beta is None else s + np.abs(beta)
+
+
+def dot_scale(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """sum_n |x[m][n] / rms_m| * |w[k][n]| for x [rows, n_in], w [n_out, n_in] (fp64)."""
+    rms = np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+    return np.abs(x / rms) @ np.abs(w).T
 
 
 def cosine(a: np.ndarray, b: np.ndarray) -> float:

@@ -137,6 +137,35 @@ def test_add_layernorm_rejects(L, args, want):
     assert L.nrs_add_layernorm(*args, None) == want
 
 
+LIN = [  # (out, x, w, rows, n_in, n_out, x_stride, w_stride, out_stride, eps, dtype)
+    ((P, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 3), DTYPE),
+    ((P, P, P, -1, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), SHAPE),
+    ((P, P, P, 5, 0, 4096, 2048, 2048, 4096, 1e-6, 1), SHAPE),
+    ((P, P, P, 5, 100, 4096, 100, 100, 4096, 1e-6, 1), SHAPE),      # not whole bf16 chunks
+    ((P, P, P, 5, (1 << 20) + 8, 16, 1 << 21, 1 << 21, 16, 1e-6, 1), SHAPE),
+    ((P, P, P, 5, 2048, 0, 2048, 2048, 16, 1e-6, 1), SHAPE),
+    ((P, P, P, 5, 2048, 1 << 31, 2048, 2048, 1 << 31, 1e-6, 1), SHAPE),
+    ((P, P, P, 5, 2048, 4096, 2040, 2048, 4096, 1e-6, 1), SHAPE),    # x stride short
+    ((P, P, P, 5, 2048, 4096, 2048, 1024, 4096, 1e-6, 1), SHAPE),    # w stride short
+    ((P, P, P, 5, 2048, 4096, 2048, 2048, 4000, 1e-6, 1), SHAPE),    # out stride short
+    ((P, P, P, 5, 2048, 4096, 2048, 2048, 4096, -1.0, 1), ARG),
+    ((P, P, P, 5, 2048, 4096, 2048, 2048, 4096, float("inf"), 0), ARG),
+    ((None, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), NULL),
+    ((P, None, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), NULL),
+    ((P, P, None, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), NULL),
+    ((P, P, U, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), ALIGN),
+    ((P, P, P, 5, 2048, 4096, 2048, 2052, 4096, 1e-6, 1), ALIGN),    # w rows not 16-byte
+    ((P + 1, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), ALIGN),  # out not element-aligned
+    ((P + 2, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 0), ALIGN),
+    ((None, None, None, 0, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), OK),
+]
+
+
+@pytest.mark.parametrize("args,want", LIN)
+def test_rmsnorm_linear_rejects(L, args, want):
+    assert L.nrs_rmsnorm_linear(*args, None) == want
+
+
 def test_binding_rejects_mixed_dtypes():
     import torch
     import norm_rope_swiglu_amd as nrs
