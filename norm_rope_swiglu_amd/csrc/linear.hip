@@ -1,4 +1,4 @@
-// Fused RMSNorm + Linear for gfx950, the decode (few-row) regime.
+// Fused RMSNorm + Linear for gfx950.
 //
 // out[m][k] = sum_n (x[m][n] / rms_m) * w[k][n],  rms_m = sqrt(mean_n x[m][n]^2 + eps)
 // ("Optimising autoregressive speech models", "Custom Triton kernels",
@@ -22,6 +22,13 @@
 // meet once in LDS.  Weights are read with ordinary cached loads: measured on
 // MI355X, nontemporal loads of this 16-rows-per-instruction pattern were up
 // to 10% slower.
+//
+// With many rows (bf16) it is a GEMM bound by the matrix cores: 256 x 256
+// output tiles of eight waves of 64 x 128 each when the problem has enough of
+// them to fill the chip, 128 x 128 tiles of four 64 x 64 waves otherwise,
+// operands staged through
+// double-buffered LDS 64 inputs at a time, and the row sums of squares taken
+// from the A fragments as the tiles stream through.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -154,6 +161,133 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
     }
 }
 
+// ---------------------------------------------------------------- many rows (GEMM)
+
+constexpr int kGBK = 64;                // inputs per LDS stage
+constexpr int kGLD = kGBK + 8;          // LDS row stride in elements: 144 bytes puts the 16
+                                        // rows read by one 16-byte fragment load on distinct banks
+
+// One workgroup of WM x WN waves computes a (16 WM TM) x (16 WN TN) tile of
+// out; wave (wm, wn) owns TM x TN MFMA tiles of 16 x 16, so every 16-byte
+// fragment read from LDS feeds TN (A) or TM (B) matrix-core steps.  Each
+// stage every thread moves 16-byte chunks of x and w from HBM into registers
+// while the waves multiply the stage already in LDS; then it writes them to
+// the other LDS buffer and all meet at one barrier.
+template <int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(64 * WM * WN) void rmsnorm_linear_gemm_kernel(
+    __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t rows, int32_t n_in, int64_t n_out,
+    int64_t x_stride, int64_t w_stride, int64_t out_stride, float inv_n, float eps,
+    uint32_t mblocks, uint32_t nblocks) {
+    constexpr int kGBM = 16 * WM * TM, kGBN = 16 * WN * TN;
+    constexpr int kGThreads = 64 * WM * WN;
+    constexpr int kGTM = TM, kGTN = TN;
+    static_assert(kGBM == kGBN, "one staging map serves both operands");
+    constexpr int kGChunks = kGBM * kGBK / 8 / kGThreads;   // 16-byte chunks per thread per operand
+    __shared__ __attribute__((aligned(16))) __bf16 As[2][kGBM * kGLD];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kGBN * kGLD];
+    __shared__ float row_ss[kGBM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int wm = wave / WN, wn = wave % WN;
+    // consecutive tiles of one XCD share a weight tile and walk down the rows
+    const uint32_t b = xcd_contiguous(blockIdx.x, mblocks * nblocks);
+    const int64_t m0 = (int64_t)(b % mblocks) * kGBM, c0 = (int64_t)(b / mblocks) * kGBN;
+    const int nstages = (n_in + kGBK - 1) / kGBK;
+    const u32x4 zero = {0, 0, 0, 0};
+
+    // staging map: chunk q = tid + threads * j is row q / 8, inputs 8 (q % 8) .. + 7
+    u32x4 ra[kGChunks], rb[kGChunks];
+    auto gload = [&](int st) {
+#pragma unroll
+        for (int j = 0; j < kGChunks; ++j) {
+            const int q = tid + kGThreads * j, row = q >> 3, n = st * kGBK + (q & 7) * 8;
+            const bool nin = n < n_in;                      // n_in is whole chunks
+            ra[j] = nin && m0 + row < rows ? load16(x + (m0 + row) * x_stride + n) : zero;
+            rb[j] = nin && c0 + row < n_out ? load16(w + (c0 + row) * w_stride + n) : zero;
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kGChunks; ++j) {
+            const int q = tid + kGThreads * j, at = (q >> 3) * kGLD + (q & 7) * 8;
+            *reinterpret_cast<u32x4 *>(&As[buf][at]) = ra[j];
+            *reinterpret_cast<u32x4 *>(&Bs[buf][at]) = rb[j];
+        }
+    };
+
+    f32x4 acc[kGTM][kGTN];
+    float ssq[kGTM];
+#pragma unroll
+    for (int i = 0; i < kGTM; ++i) {
+        ssq[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kGTN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nstages) gload(st + 1);
+#pragma unroll
+        for (int kk = 0; kk < kGBK; kk += 32) {
+            u32x4 af[kGTM], bf[kGTN];
+#pragma unroll
+            for (int t = 0; t < kGTM; ++t)
+                af[t] = *reinterpret_cast<const u32x4 *>(
+                    &As[buf][(wm * 16 * kGTM + t * 16 + r) * kGLD + kk + 8 * g]);
+#pragma unroll
+            for (int t = 0; t < kGTN; ++t)
+                bf[t] = *reinterpret_cast<const u32x4 *>(
+                    &Bs[buf][(wn * 16 * kGTN + t * 16 + r) * kGLD + kk + 8 * g]);
+            if (wn == 0) {   // one wave per row band takes the rows' sums of squares
+#pragma unroll
+                for (int t = 0; t < kGTM; ++t) {
+                    float v[8];
+                    io_traits<__bf16>::unpack(af[t], v);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ssq[t] = __builtin_fmaf(v[i], v[i], ssq[t]);
+                }
+            }
+#pragma unroll
+            for (int tm = 0; tm < kGTM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < kGTN; ++tn)
+                    acc[tm][tn] = mfma_step<__bf16>::run(af[tm], bf[tn], acc[tm][tn]);
+        }
+        if (st + 1 < nstages) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (wn == 0) {
+#pragma unroll
+        for (int t = 0; t < kGTM; ++t) {
+            float s2 = ssq[t];
+            s2 += __shfl_xor(s2, 16);
+            s2 += __shfl_xor(s2, 32);
+            if (g == 0) row_ss[wm * 16 * kGTM + t * 16 + r] = s2;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tm = 0; tm < kGTM; ++tm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * 16 * kGTM + tm * 16 + 4 * g + i;   // accumulator layout
+            const int64_t gm = m0 + row;
+            if (gm >= rows) continue;
+            const float rs = rsqrtf(__builtin_fmaf(row_ss[row], inv_n, eps));
+#pragma unroll
+            for (int tn = 0; tn < kGTN; ++tn) {
+                const int64_t gc = c0 + wn * 16 * kGTN + tn * 16 + r;
+                if (gc < n_out) out[gm * out_stride + gc] = (__bf16)(acc[tm][tn][i] * rs);
+            }
+        }
+    }
+}
+
 namespace {
 
 constexpr int kSplit = 8;      // waves per workgroup (splitting the input dimension)
@@ -177,7 +311,26 @@ hipError_t launch_typed(void *out, const void *x, const void *w, int64_t rows, i
                         int64_t n_out, int64_t xs, int64_t ws, int64_t os, float eps,
                         hipStream_t stream) {
     const float inv_n = (float)(1.0 / (double)n_in);
-    // rows beyond one launch's 64 are taken 64 at a time (each pass streams w again)
+    if (sizeof(IO) == 2 && rows > kMaxTileRows) {
+        // 256 x 256 tiles read half the operand bytes per flop of 128 x 128
+        // ones but need enough of them to give every CU one
+        const int64_t big = ((rows + 255) / 256) * ((n_out + 255) / 256);
+        const int tile = big >= 256 ? 256 : 128;
+        const uint32_t mblocks = (uint32_t)((rows + tile - 1) / tile);
+        const uint32_t nblocks = (uint32_t)((n_out + tile - 1) / tile);
+        if (tile == 256)
+            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<4, 2, 4, 8>), dim3(mblocks * nblocks),
+                               dim3(512), 0, stream, (__bf16 *)out, (const __bf16 *)x,
+                               (const __bf16 *)w, (int32_t)rows, (int32_t)n_in, n_out, xs, ws, os,
+                               inv_n, eps, mblocks, nblocks);
+        else
+            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<2, 2, 4, 4>), dim3(mblocks * nblocks),
+                               dim3(256), 0, stream, (__bf16 *)out, (const __bf16 *)x,
+                               (const __bf16 *)w, (int32_t)rows, (int32_t)n_in, n_out, xs, ws, os,
+                               inv_n, eps, mblocks, nblocks);
+        return hipGetLastError();
+    }
+    // fp32 rows beyond one launch's 64 are taken 64 at a time (each pass streams w again)
     for (int64_t m0 = 0; m0 < rows; m0 += kMaxTileRows) {
         const int32_t mr = (int32_t)(rows - m0 < kMaxTileRows ? rows - m0 : kMaxTileRows);
         IO *o = (IO *)out + m0 * os;

@@ -114,6 +114,28 @@ def test_eps_dominated_and_zero_rows(dt):
     lin_parity(x, w, 0.0, f"lin/{dt}/eps0_nonzero_rows", rows=torch.tensor([0, 1, 3, 4, 5]))
 
 
+@pytest.mark.parametrize("rows,n_in,n_out", [(65, 64, 128), (129, 200, 200), (300, 1000, 130),
+                                             (257, 8, 16), (512, 2048, 384)])
+def test_gemm_tile_tails(rows, n_in, n_out):
+    # the many-row (tiled) path: row, input and output counts off the 128 x 128 x 64 tiles
+    x, w = lin_inputs(rows, n_in, n_out, "bf16", 10)
+    lin_parity(x, w, 1e-6, f"lin/gemm/{rows}x{n_in}x{n_out}")
+
+
+def test_gemm_big_tiles_with_tails():
+    # >= 256 tiles of 256 x 256 (the large-tile path), row and column counts off the tile
+    x, w = lin_inputs(4100, 1000, 4100, "bf16", 12)
+    g = torch.Generator().manual_seed(13)
+    rows = torch.unique(torch.cat([torch.tensor([0, 255, 256, 4095, 4096, 4099]),
+                                   torch.randint(0, 4100, (40,), generator=g)]))
+    lin_parity(x, w, 1e-6, "lin/gemm/big4100", rows=rows)
+
+
+def test_gemm_strided_operands():
+    xb, wb = lin_inputs(200, 640, 96, "bf16", 11)
+    lin_parity(xb[:, 64:576], wb[:, 128:640], 1e-6, "lin/gemm/strided")
+
+
 def test_wide_vocab_head():
     x, w = lin_inputs(2, 1024, 32000, "bf16", 7)
     lin_parity(x, w, 1e-6, "lin/vocab32000")
