@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0
 METRIC = "achieved HBM GB/s (% of peak) per fused op; µs per decode-step op set"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_prefill32k_bf16.json")
 KERNEL_SOURCES = ["norm_rope_swiglu_amd/csrc/swiglu.hip", "norm_rope_swiglu_amd/csrc/device.hpp"]
@@ -361,6 +362,13 @@ def main():
             "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del ws, graph
+    # the prefill shape: 2048 tokens x 2048 -> 4096 (qkv), bound by the matrix cores
+    lin_xp = torch.empty(2048, H, device=dev).normal_().to(torch.bfloat16)
+    lin_wp = torch.empty(4096, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
+    lin_yp = torch.empty(2048, 4096, dtype=torch.bfloat16, device=dev)
+    nxt["rmsnorm_linear_2048x2048x4096"] = (
+        lambda: nrs.rmsnorm_linear(lin_xp, lin_wp, 1e-6, out=lin_yp),
+        2048 * H * 2 + 4096 * H * 2 + 2048 * 4096 * 2)
     for op, (fn, byts) in nxt.items():
         for _ in range(3):
             fn()
@@ -377,8 +385,13 @@ def main():
         next_ops[op] = {"mean_us": round(mean_us, 2), "bytes": byts,
                         "GB_s": round(byts / (mean_us * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(byts / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        if op.startswith("rmsnorm_linear_2048"):   # a contraction: priced against the bf16 MFMA peak
+            tf = 2 * 2048 * H * 4096 / (mean_us * 1e-6) / 1e12
+            next_ops[op] = {"mean_us": round(mean_us, 2), "TFLOP_s": round(tf, 1),
+                            "frac_of_peak": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                            "peak": "bf16 dense MFMA 2500 TFLOP/s"}
     next_ops.update(lin)
-    del v, kc, vc, lg_dec, lg_big
+    del v, kc, vc, lg_dec, lg_big, lin_xp, lin_wp, lin_yp
     print(f"bench: next {json.dumps(next_ops)}", file=sys.stderr, flush=True)
 
     sw = per_op["swiglu"]
