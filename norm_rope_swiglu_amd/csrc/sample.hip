@@ -15,14 +15,20 @@
 //   1. radix select of the k-th largest logit on monotone 32-bit keys, 8 bits
 //      per pass (4 passes for fp32, 2 for bf16, whose low 16 key bits are
 //      fixed by the sign), histograms in LDS;
-//   2. an ordered compaction pass gathers every logit above that key and the
-//      lowest-index ties (a block-wide prefix count keeps ties in index order);
-//   3. a bitonic sort of the (at most 1024) kept entries in LDS by (logit
-//      descending, index ascending);
+//   2. one pass gathers every logit above that key and every tie at it (the
+//      histogram counts them) when they fit the 1024-entry buffer; only
+//      longer tie runs take an ordered compaction (a block-wide prefix count
+//      per 1024 chunks keeps the lowest-index ties);
+//   3. a sort of the gathered entries by (logit descending, index ascending):
+//      lane exchanges within one wave for up to 64, a bitonic network in LDS
+//      beyond;
 //   4. exp((l - l_max) / T) per kept entry, an inclusive block scan, and the
 //      first entry whose prefix exceeds u * total.
-// Every pass reads the row with 16-byte loads; the row is re-read from the
-// caches between passes.
+// Rows of up to 8 16-byte chunks per thread (65536 bf16 or 32768 fp32
+// logits) are read from HBM once, into registers, as order keys, and every
+// pass runs over the registers; longer rows are re-read (from the caches) by
+// each pass.  (At 20 chunks per thread the registers spill and the kernel
+// ran slower than streaming the row.)
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -45,6 +51,41 @@ __device__ inline float value_of(uint32_t k) {
     const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
     return __builtin_bit_cast(float, b);
 }
+
+// Rows are held as order keys: an fp32 chunk as four 32-bit keys, a bf16
+// chunk as eight 16-bit keys (the high half of the fp32 key; its low half
+// follows from the sign), two to a word, so a chunk keeps its 16 bytes.
+template <typename IO> struct keys;
+
+template <> struct keys<float> {
+    static constexpr int VEC = 4;
+    __device__ static inline u32x4 from_raw(const u32x4 &raw) {
+        u32x4 k;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = key_of(__builtin_bit_cast(float, (unsigned)raw[i]));
+        return k;
+    }
+    __device__ static inline uint32_t at(const u32x4 &k, int e) { return k[e]; }
+};
+
+template <> struct keys<__bf16> {
+    static constexpr int VEC = 8;
+    __device__ static inline uint32_t key16(uint32_t h) {
+        if (h == 0x8000u) h = 0u;                       // -0 onto +0
+        return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+    }
+    __device__ static inline u32x4 from_raw(const u32x4 &raw) {
+        u32x4 k;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            k[i] = key16(raw[i] & 0xFFFFu) | (key16(raw[i] >> 16) << 16);
+        return k;
+    }
+    __device__ static inline uint32_t at(const u32x4 &k, int e) {
+        const uint32_t h = (k[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        return (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);   // the full fp32 key
+    }
+};
 
 // Exclusive prefix over the block (thread order) of a small int, and the total.
 __device__ inline int block_exclusive_scan(int v, int *wave_tot, int &total) {
@@ -87,16 +128,19 @@ __device__ inline float block_inclusive_scan(float v, float *wave_tot) {
 }
 }  // namespace
 
-template <typename IO>
+// CPT > 0: thread t holds the row's chunks t, t + 1024, ... (at most CPT of
+// them) in registers; CPT == 0: every pass streams the row from memory.
+template <typename IO, int CPT>
 __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     int32_t *token, IO *probs, const IO *logits, int64_t vocab, int64_t row_stride,
     int64_t probs_stride, float inv_temp, int32_t top_k, const float *u) {
+    using K = keys<IO>;
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
     constexpr int NPASS = sizeof(IO) == 4 ? 4 : 2;
     __shared__ uint32_t hist[256 * 32];   // 256 digits x 32 bank replicas
     __shared__ uint32_t wtot[4];
-    __shared__ uint32_t sel[2];            // selected digit, count strictly above it
+    __shared__ uint32_t sel[3];            // selected digit, count above it, count equal
     __shared__ int iscan[kWaves];
     __shared__ float fscan[kWaves];
     __shared__ uint32_t ckey[kThreads];    // kept entries: key and index
@@ -110,6 +154,54 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     const IO *x = logits + row * row_stride;
     const int64_t nchunks = vocab / VEC;
 
+    // the row's source: keys in registers (loaded here, all at once) or
+    // memory (converted to keys as each pass reads it)
+    u32x4 held[CPT > 0 ? CPT : 1];
+    if constexpr (CPT > 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int64_t c = tid + (int64_t)j * kThreads;
+            if (c < nchunks) held[j] = load16(x + c * VEC);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) held[j] = K::from_raw(held[j]);
+    }
+    // Marks the held keys as rewritten (an empty asm statement that emits no
+    // instruction), so each pass re-derives per-element keys from them instead
+    // of the compiler keeping every pass's unpacked keys alive in registers.
+    auto opaque = [&]() {
+        if constexpr (CPT > 0) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(held[j][i]));
+        }
+    };
+    // f(c, keys) for every chunk c this thread owns, in increasing c
+    auto for_chunks = [&](auto &&f) {
+        if constexpr (CPT > 0) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int64_t c = tid + (int64_t)j * kThreads;
+                if (c < nchunks) f(c, held[j]);
+            }
+        } else {
+            for (int64_t c0 = tid; c0 < nchunks; c0 += kUnroll * kThreads) {
+                u32x4 raw[kUnroll];
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const int64_t c = c0 + j * kThreads;
+                    if (c < nchunks) raw[j] = load16(x + c * VEC);
+                }
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const int64_t c = c0 + j * kThreads;
+                    if (c < nchunks) f(c, K::from_raw(raw[j]));
+                }
+            }
+        }
+    };
+
     // 1. radix select: find the top_k-th largest key.  Each bin is replicated
     //    across the 32 LDS banks (indexed by lane) so lanes counting the same
     //    digit, common with peaky logits, rarely hit one address.
@@ -119,27 +211,16 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     for (int pass = 0; pass < NPASS; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < 256 * 32; i += kThreads) hist[i] = 0;
+        opaque();
         __syncthreads();
-        for (int64_t c0 = tid; c0 < nchunks; c0 += kUnroll * kThreads) {
-            u32x4 raw[kUnroll];
+        for_chunks([&](int64_t, const u32x4 &kc) {
 #pragma unroll
-            for (int j = 0; j < kUnroll; ++j) {
-                const int64_t c = c0 + j * kThreads;
-                if (c < nchunks) raw[j] = load16(x + c * VEC);
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t key = K::at(kc, e);
+                if ((key & pmask) == prefix)
+                    atomicAdd(&hist[((key >> shift) & 255u) * 32 + rep], 1u);
             }
-#pragma unroll
-            for (int j = 0; j < kUnroll; ++j) {
-                if (c0 + j * kThreads >= nchunks) break;
-                float v[VEC];
-                T::unpack(raw[j], v);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const uint32_t key = key_of(v[e]);
-                    if ((key & pmask) == prefix)
-                        atomicAdd(&hist[((key >> shift) & 255u) * 32 + rep], 1u);
-                }
-            }
-        }
+        });
         __syncthreads();
         // thread t < 256 sums digit 255 - t (rotating the replica index keeps
         // the 64 lanes of a wave on different banks); an inclusive scan over t
@@ -164,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
             if (incl - h < need && need <= incl) {  // the need-th largest has digit d
                 sel[0] = d;
                 sel[1] = incl - h;
+                sel[2] = h;
             }
         }
         __syncthreads();
@@ -177,23 +259,43 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     const uint32_t kth = prefix;
     const uint32_t kth_mask = pmask;
     const int n_above = top_k - (int)need;   // keys strictly above kth
+    const int n_tied = (int)sel[2];          // keys equal to kth (the last pass's bin)
 
-    // 2. ordered compaction of the kept entries
+    // 2. gather the kept entries.  When everything above kth and every tie at
+    //    kth fits the 1024-entry buffer, one pass appends them all in any
+    //    order and the sort below ranks the ties by index; otherwise an
+    //    ordered compaction keeps exactly the lowest-index `need` ties.
     if (tid == 0) n_gt = 0;
     __syncthreads();
-    int eq_taken = 0;
-    for (int64_t base = 0; base < nchunks; base += kThreads) {
-        const int64_t c = base + tid;
-        float v[VEC];
-        int n_eq = 0;
-        if (c < nchunks) {
-            T::unpack(load16(x + c * VEC), v);
+    const bool gather_all = n_above + n_tied <= kThreads;
+    const int n_kept = gather_all ? n_above + n_tied : top_k;   // entries to sort
+    if (gather_all) {
+        opaque();
+        for_chunks([&](int64_t c, const u32x4 &kc) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const uint32_t key = key_of(v[e]) & kth_mask;
+                const uint32_t full = K::at(kc, e);
+                if ((full & kth_mask) >= kth) {
+                    const uint32_t at = atomicAdd(&n_gt, 1u);
+                    ckey[at] = full;
+                    cidx[at] = (int32_t)(c * VEC + e);
+                }
+            }
+        });
+    } else {
+    int eq_taken = 0;
+    opaque();
+    // one block-wide step per 1024 chunks, so ties are ranked in index order
+    auto compact = [&](int64_t base, const u32x4 &kc) {
+        const int64_t c = base + tid;
+        int n_eq = 0;
+        if (c < nchunks) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t full = K::at(kc, e), key = full & kth_mask;
                 if (key > kth) {
                     const uint32_t at = atomicAdd(&n_gt, 1u);
-                    ckey[at] = key_of(v[e]);
+                    ckey[at] = full;
                     cidx[at] = (int32_t)(c * VEC + e);
                 } else if (key == kth) {
                     ++n_eq;
@@ -205,9 +307,10 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         if (c < nchunks && n_eq > 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                if ((key_of(v[e]) & kth_mask) == kth) {
+                const uint32_t full = K::at(kc, e);
+                if ((full & kth_mask) == kth) {
                     if (r < (int)need) {
-                        ckey[n_above + r] = key_of(v[e]);
+                        ckey[n_above + r] = full;
                         cidx[n_above + r] = (int32_t)(c * VEC + e);
                     }
                     ++r;
@@ -215,35 +318,74 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
             }
         }
         eq_taken += chunk_total;
+    };
+    if constexpr (CPT > 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            if ((int64_t)j * kThreads >= nchunks) break;   // uniform: every thread stops together
+            compact((int64_t)j * kThreads, held[j]);
+        }
+    } else {
+        for (int64_t base = 0; base < nchunks; base += kThreads) {
+            const int64_t c = base + tid;
+            compact(base, c < nchunks ? K::from_raw(load16(x + c * VEC)) : u32x4{0, 0, 0, 0});
+        }
     }
+    }   // ordered compaction
     __syncthreads();
 
-    // 3. bitonic sort of the kept entries: logit descending, index ascending
+    // 3. bitonic sort of the kept entries: logit descending, index ascending.
+    //    Up to 64 entries are sorted by the first wave alone with lane
+    //    exchanges (no barrier); more go through LDS with a barrier per step.
     int n = 1;
-    while (n < top_k) n <<= 1;
-    if (tid >= top_k && tid < n) {
-        ckey[tid] = 0u;          // below every real key
-        cidx[tid] = 0x7FFFFFFF;
-    }
-    __syncthreads();
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (tid < n) {
-                const int other = tid ^ stride;
-                if (other > tid) {
-                    const uint32_t ka = ckey[tid], kb = ckey[other];
-                    const int32_t ia = cidx[tid], ib = cidx[other];
-                    const bool a_first = ka > kb || (ka == kb && ia < ib);
-                    const bool up = (tid & size) == 0;
-                    if (up != a_first) {
-                        ckey[tid] = kb;
-                        ckey[other] = ka;
-                        cidx[tid] = ib;
-                        cidx[other] = ia;
+    while (n < n_kept) n <<= 1;
+    if (n <= 64) {
+        if (tid < 64) {
+            uint32_t k = tid < n_kept ? ckey[tid] : 0u;          // below every real key
+            int32_t ix = tid < n_kept ? cidx[tid] : 0x7FFFFFFF;
+            for (int size = 2; size <= 64; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    const uint32_t ko = __shfl_xor(k, stride, 64);
+                    const int32_t io = __shfl_xor(ix, stride, 64);
+                    // the lower lane of each pair keeps the first of the two in
+                    // the pair's direction (descending when (tid & size) == 0)
+                    const bool mine_first = k > ko || (k == ko && ix < io);
+                    const bool lower = (tid & stride) == 0, up = (tid & size) == 0;
+                    if (mine_first != (lower == up)) {
+                        k = ko;
+                        ix = io;
                     }
                 }
             }
-            __syncthreads();
+            ckey[tid] = k;
+            cidx[tid] = ix;
+        }
+        __syncthreads();
+    } else {
+        if (tid >= n_kept && tid < n) {
+            ckey[tid] = 0u;          // below every real key
+            cidx[tid] = 0x7FFFFFFF;
+        }
+        __syncthreads();
+        for (int size = 2; size <= n; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                if (tid < n) {
+                    const int other = tid ^ stride;
+                    if (other > tid) {
+                        const uint32_t ka = ckey[tid], kb = ckey[other];
+                        const int32_t ia = cidx[tid], ib = cidx[other];
+                        const bool a_first = ka > kb || (ka == kb && ia < ib);
+                        const bool up = (tid & size) == 0;
+                        if (up != a_first) {
+                            ckey[tid] = kb;
+                            ckey[other] = ka;
+                            cidx[tid] = ib;
+                            cidx[other] = ia;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
         }
     }
 
@@ -265,13 +407,12 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
 
     // optional full softmax row
     if (probs) {
+        opaque();
         float part = 0.0f;
-        for (int64_t c = tid; c < nchunks; c += kThreads) {
-            float v[VEC];
-            T::unpack(load16(x + c * VEC), v);
+        for_chunks([&](int64_t, const u32x4 &kc) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) part += expf((v[e] - lmax) * inv_temp);
-        }
+            for (int e = 0; e < VEC; ++e) part += expf((value_of(K::at(kc, e)) - lmax) * inv_temp);
+        });
         part = wave_sum(part);
         if ((tid & 63) == 0) fscan[tid >> 6] = part;
         __syncthreads();
@@ -280,30 +421,54 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         for (int wv = 0; wv < kWaves; ++wv) tot += fscan[wv];
         const float inv = 1.0f / tot;
         IO *p = probs + row * probs_stride;
-        for (int64_t c = tid; c < nchunks; c += kThreads) {
-            float v[VEC], o[VEC];
-            T::unpack(load16(x + c * VEC), v);
+        for_chunks([&](int64_t c, const u32x4 &kc) {
+            float o[VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[e] = expf((v[e] - lmax) * inv_temp) * inv;
+            for (int e = 0; e < VEC; ++e) o[e] = expf((value_of(K::at(kc, e)) - lmax) * inv_temp) * inv;
             store16(p + c * VEC, T::pack(o));
-        }
+        });
     }
 }
+
+namespace {
+
+template <typename IO, int CPT>
+void launch_cpt(int32_t *token, void *probs, const void *logits, int64_t rows, int64_t vocab,
+                int64_t row_stride, int64_t probs_stride, float inv_temp, int32_t top_k,
+                const float *u, hipStream_t stream) {
+    hipLaunchKernelGGL((topk_sample_kernel<IO, CPT>), dim3((unsigned)rows), dim3(kThreads), 0,
+                       stream, token, (IO *)probs, (const IO *)logits, vocab, row_stride,
+                       probs_stride, inv_temp, top_k, u);
+}
+
+template <typename IO>
+void launch_typed(int32_t *token, void *probs, const void *logits, int64_t rows, int64_t vocab,
+                  int64_t row_stride, int64_t probs_stride, float inv_temp, int32_t top_k,
+                  const float *u, hipStream_t stream) {
+    const int64_t per_thread = (vocab / io_traits<IO>::VEC + kThreads - 1) / kThreads;
+#define NRS_TS(C) launch_cpt<IO, C>(token, probs, logits, rows, vocab, row_stride, probs_stride, \
+                                    inv_temp, top_k, u, stream)
+    if (per_thread <= 1) NRS_TS(1);
+    else if (per_thread <= 2) NRS_TS(2);
+    else if (per_thread <= 4) NRS_TS(4);
+    else if (per_thread <= 8) NRS_TS(8);
+    else NRS_TS(0);
+#undef NRS_TS
+}
+
+}  // namespace
 
 hipError_t launch_topk_sample(int32_t *token, void *probs, const void *logits, int64_t rows,
                               int64_t vocab, int64_t row_stride, int64_t probs_stride,
                               float temperature, int32_t top_k, const float *u, int dtype,
                               hipStream_t stream) {
-    const dim3 grid((unsigned)rows), block(kThreads);
     const float inv_temp = (float)(1.0 / (double)temperature);
     if (dtype == 0)
-        hipLaunchKernelGGL(topk_sample_kernel<float>, grid, block, 0, stream, token,
-                           (float *)probs, (const float *)logits, vocab, row_stride, probs_stride,
-                           inv_temp, top_k, u);
+        launch_typed<float>(token, probs, logits, rows, vocab, row_stride, probs_stride, inv_temp,
+                            top_k, u, stream);
     else
-        hipLaunchKernelGGL(topk_sample_kernel<__bf16>, grid, block, 0, stream, token,
-                           (__bf16 *)probs, (const __bf16 *)logits, vocab, row_stride,
-                           probs_stride, inv_temp, top_k, u);
+        launch_typed<__bf16>(token, probs, logits, rows, vocab, row_stride, probs_stride, inv_temp,
+                             top_k, u, stream);
     return hipGetLastError();
 }
 

@@ -183,6 +183,14 @@ def test_sample_ties(dt):
     tok, _ = sample_parity(lg, 1.0, 16, torch.tensor([0.0, 0.5, 0.99], dtype=torch.float32),
                            f"sample/flat/{dt}")
     assert tok.tolist() == [0, 8, 15]
+    # ties at the k-th value outnumbering the 1024-entry gather buffer: the ordered
+    # compaction must keep the lowest indices (a few larger logits sit above them)
+    lg = torch.zeros(3, 8192)
+    lg[:, [5000, 7, 8191]] = torch.tensor([3.0, 2.0, 1.0])
+    lg = lg.to(W.store(torch.zeros(1), dt).dtype)
+    tok, _ = sample_parity(lg, 1.0, 20, torch.tensor([0.0, 0.9999, 0.97], dtype=torch.float32),
+                           f"sample/many_ties/{dt}")
+    assert tok[0] == 5000
 
 
 def test_sample_greedy_is_first_argmax():
