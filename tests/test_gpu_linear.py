@@ -157,3 +157,9 @@ def test_empty_and_rejects():
     with pytest.raises(ValueError):
         nrs.rmsnorm_linear(torch.empty(4, 256, dtype=torch.bfloat16, device="cuda"),
                            torch.empty(64, 128, dtype=torch.bfloat16, device="cuda"))
+
+
+def test_fp32_many_rows_in_64_row_passes():
+    # fp32 rows beyond 64 go through the few-row kernel 64 rows at a time
+    x, w = lin_inputs(150, 512, 80, "f32", 14)
+    lin_parity(x, w, 1e-6, "lin/f32/rows150")
