@@ -1,7 +1,8 @@
 /*
  * libnrs: fused per-token decoder-layer ops (RMSNorm, residual-add + RMSNorm,
  * M-RoPE, SwiGLU) as hand-written HIP kernels for AMD CDNA4 (gfx950), behind
- * a plain C ABI.
+ * a plain C ABI; beyond them, M-RoPE fused with the KV-cache append, softmax +
+ * top-k sampling, LayerNorm, and RMSNorm fused into a Linear.
  *
  * Conventions for every entry point below:
  *   - Tensor pointers are DEVICE pointers; sizes and strides count ELEMENTS;
@@ -18,7 +19,7 @@
  *   - Errors: a negative nrs_status.  Argument checks run on the host before
  *     any HIP call, so an invalid call touches neither the GPU nor its
  *     buffers.  A zero-sized call (rows or tokens == 0) returns NRS_OK and
- *     launches nothing.  NRS_ERR_HIP means the launch itself failed;
+ *     launches nothing; rows and tokens above 2^31 - 1 return NRS_ERR_SHAPE.  NRS_ERR_HIP means the launch itself failed;
  *     nrs_last_hip_error() then gives the hipError_t of this thread's call.
  *   - Pointers must be 16-byte aligned and strides must span whole 16-byte
  *     chunks (NRS_ERR_ALIGN otherwise).  Buffers may not overlap except where

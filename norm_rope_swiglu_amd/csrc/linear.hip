@@ -322,18 +322,25 @@ hipError_t launch_typed(void *out, const void *x, const void *w, int64_t rows, i
         // ones but need enough of them to give every CU one
         const int64_t big = ((rows + 255) / 256) * ((n_out + 255) / 256);
         const int tile = big >= 256 ? 256 : 128;
-        const uint32_t mblocks = (uint32_t)((rows + tile - 1) / tile);
         const uint32_t nblocks = (uint32_t)((n_out + tile - 1) / tile);
-        if (tile == 256)
-            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<4, 2, 4, 8>), dim3(mblocks * nblocks),
-                               dim3(512), 0, stream, (__bf16 *)out, (const __bf16 *)x,
-                               (const __bf16 *)w, (int32_t)rows, (int32_t)n_in, n_out, xs, ws, os,
-                               inv_n, eps, mblocks, nblocks);
-        else
-            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<2, 2, 4, 4>), dim3(mblocks * nblocks),
-                               dim3(256), 0, stream, (__bf16 *)out, (const __bf16 *)x,
-                               (const __bf16 *)w, (int32_t)rows, (int32_t)n_in, n_out, xs, ws, os,
-                               inv_n, eps, mblocks, nblocks);
+        // rows per launch: whole tiles, and a grid below 2^31 workgroups
+        const int64_t max_mblocks = (((int64_t)1 << 31) - 1) / nblocks;
+        for (int64_t r0 = 0; r0 < rows; r0 += max_mblocks * tile) {
+            const int64_t rr = rows - r0 < max_mblocks * tile ? rows - r0 : max_mblocks * tile;
+            const uint32_t mblocks = (uint32_t)((rr + tile - 1) / tile);
+            __bf16 *o = (__bf16 *)out + r0 * os;
+            const __bf16 *xx = (const __bf16 *)x + r0 * xs;
+            if (tile == 256)
+                hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<4, 2, 4, 8>),
+                                   dim3(mblocks * nblocks), dim3(512), 0, stream, o, xx,
+                                   (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out, xs, ws,
+                                   os, inv_n, eps, mblocks, nblocks);
+            else
+                hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<2, 2, 4, 4>),
+                                   dim3(mblocks * nblocks), dim3(256), 0, stream, o, xx,
+                                   (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out, xs, ws,
+                                   os, inv_n, eps, mblocks, nblocks);
+        }
         return hipGetLastError();
     }
     // fp32 rows beyond one launch's 64 are taken 64 at a time (each pass streams w again)

@@ -12,6 +12,8 @@ namespace nrs {
 // Widest rows: 512 threads x 16 chunks of 16 bytes (block-per-row kernel).
 constexpr int64_t kMaxHiddenBytes = (int64_t)512 * 16 * 16;
 constexpr int kMaxHeadDim = 512;
+// Row and token counts reach the kernels as 32-bit values and grid sizes.
+constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1;
 constexpr int64_t kMaxHeads = 1 << 16;
 
 inline int elem_size(int dtype) { return dtype == NRS_F32 ? 4 : 2; }
@@ -24,7 +26,7 @@ inline int check_rmsnorm(const void *y, const void *x, const void *gamma, int64_
                          int64_t hidden, int64_t x_stride, int64_t y_stride, float eps,
                          int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
-    if (rows < 0 || hidden <= 0 || hidden % vec_of(dtype) != 0 ||
+    if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden % vec_of(dtype) != 0 ||
         hidden * elem_size(dtype) > kMaxHiddenBytes)
         return NRS_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return NRS_ERR_ARG;
@@ -70,7 +72,7 @@ inline int check_mrope(const void *q, const void *k, const int32_t *pos, int64_t
                        int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_h,
                        int32_t sec_w, double theta, int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
-    if (tokens < 0 || n_q < 0 || n_kv < 0 || (int64_t)n_q + n_kv > kMaxHeads)
+    if (tokens < 0 || tokens > kMaxRows || n_q < 0 || n_kv < 0 || (int64_t)n_q + n_kv > kMaxHeads)
         return NRS_ERR_SHAPE;
     if (head_dim <= 0 || head_dim > kMaxHeadDim || head_dim % (2 * vec_of(dtype)) != 0)
         return NRS_ERR_SHAPE;
@@ -115,7 +117,8 @@ inline int check_mrope_kv(const void *q, const void *k, const void *v, const int
 inline int check_swiglu(const void *out, const void *gate_up, int64_t rows, int64_t inter,
                         int64_t gate_up_stride, int64_t out_stride, int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
-    if (rows < 0 || inter <= 0 || inter % vec_of(dtype) != 0 || inter / vec_of(dtype) >= (1 << 30))
+    if (rows < 0 || rows > kMaxRows || inter <= 0 || inter % vec_of(dtype) != 0 ||
+        inter / vec_of(dtype) >= (1 << 30))
         return NRS_ERR_SHAPE;
     if (rows == 0) return NRS_OK;
     if (gate_up_stride < 2 * inter || out_stride < inter) return NRS_ERR_SHAPE;
@@ -133,7 +136,8 @@ inline int check_rmsnorm_linear(const void *out, const void *x, const void *w, i
                                 int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
                                 int64_t out_stride, float eps, int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
-    if (rows < 0 || n_in <= 0 || n_in % vec_of(dtype) != 0 || n_in > kMaxLinearIn || n_out <= 0 ||
+    if (rows < 0 || rows > kMaxRows || n_in <= 0 || n_in % vec_of(dtype) != 0 ||
+        n_in > kMaxLinearIn || n_out <= 0 ||
         n_out >= kMaxLinearOut)
         return NRS_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return NRS_ERR_ARG;
@@ -153,7 +157,8 @@ inline int check_topk_sample(const int32_t *token, const void *probs, const void
                              int64_t rows, int64_t vocab, int64_t row_stride, int64_t probs_stride,
                              float temperature, int32_t top_k, const float *u, int dtype) {
     if (!known_dtype(dtype)) return NRS_ERR_DTYPE;
-    if (rows < 0 || vocab <= 0 || vocab % vec_of(dtype) != 0 || vocab >= ((int64_t)1 << 31))
+    if (rows < 0 || rows > kMaxRows || vocab <= 0 || vocab % vec_of(dtype) != 0 ||
+        vocab >= ((int64_t)1 << 31))
         return NRS_ERR_SHAPE;
     if (top_k < 1 || top_k > kMaxTopK || top_k > vocab) return NRS_ERR_ARG;
     if (!(temperature > 0.0f) || isinf(temperature)) return NRS_ERR_ARG;

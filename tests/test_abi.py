@@ -79,6 +79,7 @@ RMS = [  # (y, x, gamma, rows, hidden, x_stride, y_stride, eps, dtype) -> status
     ((P, P, U, 4, 256, 256, 256, 1e-6, 1), ALIGN),
     ((P, P, P, 4, 256, 258, 256, 1e-6, 0), ALIGN),        # fp32 stride of 1032 bytes
     ((None, None, None, 0, 256, 256, 256, 1e-6, 1), OK),  # empty: nothing launched
+    ((P, P, P, 1 << 31, 256, 256, 256, 1e-6, 1), SHAPE),  # more rows than 32-bit grids take
 ]
 
 
@@ -158,6 +159,7 @@ LIN = [  # (out, x, w, rows, n_in, n_out, x_stride, w_stride, out_stride, eps, d
     ((P + 1, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), ALIGN),  # out not element-aligned
     ((P + 2, P, P, 5, 2048, 4096, 2048, 2048, 4096, 1e-6, 0), ALIGN),
     ((None, None, None, 0, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), OK),
+    ((P, P, P, 1 << 31, 2048, 4096, 2048, 2048, 4096, 1e-6, 1), SHAPE),
 ]
 
 
@@ -204,6 +206,7 @@ MROPE = [
     (mr(q=U), ALIGN),
     (mr(qs=260), ALIGN),
     (mr(q=None, k=None, pos=None, tokens=0), OK),
+    (mr(tokens=1 << 31, pos_stride=1 << 31), SHAPE),
     (mr(q=None, k=None, pos=None, nq=0, nkv=0), OK),
 ]
 
@@ -248,6 +251,7 @@ def test_mrope_kv_append_rejects(L, args, want):
 TS = [  # (token, probs, logits, rows, vocab, row_stride, probs_stride, temperature, top_k, u, dtype)
     ((P, None, P, 4, 3072, 3072, 0, 1.0, 50, P, 2), DTYPE),
     ((P, None, P, -1, 3072, 3072, 0, 1.0, 50, P, 1), SHAPE),
+    ((P, None, P, 1 << 31, 3072, 3072, 0, 1.0, 50, P, 1), SHAPE),
     ((P, None, P, 4, 3070, 3070, 0, 1.0, 50, P, 1), SHAPE),       # not a multiple of 8 bf16
     ((P, None, P, 4, 3072, 3072, 0, 1.0, 0, P, 1), ARG),
     ((P, None, P, 4, 3072, 3072, 0, 1.0, 1025, P, 1), ARG),
@@ -275,6 +279,7 @@ def test_softmax_topk_sample_rejects(L, args, want):
 SWIGLU = [  # (out, gate_up, rows, inter, gate_up_stride, out_stride, dtype)
     ((P, P, 4, 768, 1536, 768, 9), DTYPE),
     ((P, P, -2, 768, 1536, 768, 1), SHAPE),
+    ((P, P, 1 << 31, 768, 1536, 768, 1), SHAPE),
     ((P, P, 4, 0, 1536, 768, 1), SHAPE),
     ((P, P, 4, 764, 1528, 764, 1), SHAPE),
     ((P, P, 4, 768, 1535, 768, 1), SHAPE),
