@@ -174,6 +174,16 @@ def test_sample_decode_rows(dt, vocab, k, scale, T):
     sample_parity(lg, T, k, _u(rows, 2), f"sample/{dt}/V{vocab}/k{k}")
 
 
+@pytest.mark.parametrize("dt,vocab", [("bf16", 16384), ("bf16", 32000), ("bf16", 65536),
+                                      ("f32", 8192), ("f32", 16384), ("f32", 32000),
+                                      ("bf16", 65544), ("f32", 32776)])
+def test_sample_register_held_rows(dt, vocab):
+    # rows held in registers at 2, 4 and 8 chunks per thread, and just past the
+    # largest held row (streamed by every pass)
+    lg = _logits(6, vocab, 3.0, dt, 11)
+    sample_parity(lg, 0.8, 64, _u(6, 12), f"sample/{dt}/held{vocab}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_sample_ties(dt):
     # integer-valued logits: many equal values, the k-th often tied
