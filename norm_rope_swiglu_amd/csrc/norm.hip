@@ -32,24 +32,39 @@
 
 namespace nrs {
 
+// Sum over aligned groups of SEG lanes (SEG a power of two up to 32): every
+// lane of a group ends with its group's sum.
+template <int SEG> __device__ inline float seg_sum(float v) {
+#pragma unroll
+    for (int o = SEG / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 // A row is split over WPR waves of 64 threads; each thread holds NCH chunks
 // (thread t of the row owns chunks t, t + 64*WPR, ...).  Rows of one wave are
-// packed four to a block, wider rows get a block each.
+// packed four to a block, wider rows get a block each.  Rows of at most 32
+// chunks (SEG < 64, e.g. per-head norms over head_dim) share a wave: each
+// takes an aligned group of SEG lanes (the chunk count rounded up to a power
+// of two), so a 256-thread block holds 256 / SEG rows and no wave idles on a
+// short row.
 // LN selects LayerNorm (beta may be null) over RMSNorm.
-template <typename IO, int WPR, int NCH, bool ADD, bool LN, bool NT>
+template <typename IO, int WPR, int NCH, bool ADD, bool LN, bool NT, int SEG = 64>
 __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
     IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, const IO *beta,
     int64_t rows, int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    constexpr int RPB = WPR == 1 ? 4 : 1;      // rows per block
-    constexpr int TPR = 64 * WPR;               // threads per row
+    static_assert(SEG == 64 || (WPR == 1 && NCH == 1), "short rows take one chunk per lane");
+    constexpr int TPR = SEG < 64 ? SEG : 64 * WPR;                     // threads per row
+    constexpr int RPB = SEG < 64 ? 256 / SEG : (WPR == 1 ? 4 : 1);     // rows per block
     __shared__ float partial[LN ? 1 : WPR * RPB];
     __shared__ float4 moments[LN ? WPR * RPB : 1];
 
     const int wave = threadIdx.x >> 6;
-    const int rib = wave / WPR;                 // row within the block
+    const int rib = threadIdx.x / TPR;          // row within the block
     const int t = threadIdx.x - rib * TPR;      // thread within the row
+    // a row's reduction: its lane group, or the whole wave (and LDS beyond)
+    auto row_sum = [](float v) { return SEG < 64 ? seg_sum<SEG < 64 ? SEG : 1>(v) : wave_sum(v); };
     const int64_t row = (int64_t)blockIdx.x * RPB + rib;
     const bool live = row < rows;
 
@@ -93,7 +108,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
 #pragma unroll
         for (int i = 0; i < VEC; ++i) ss = LN ? ss + v[i] : __builtin_fmaf(v[i], v[i], ss);
     }
-    ss = wave_sum(ss);
+    ss = row_sum(ss);
     float mean = 0.0f;
     if (!LN) {
         if (WPR > 1) {
@@ -112,7 +127,8 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
         const int wir = wave - rib * WPR;       // wave within the row
         int nw = 0;                             // elements held by this wave
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) nw += min(max(nchunks - TPR * c - 64 * wir, 0), 64);
+        for (int c = 0; c < NCH; ++c)
+            nw += SEG < 64 ? nchunks : min(max(nchunks - TPR * c - 64 * wir, 0), 64);
         nw *= VEC;
         const float mw = nw > 0 ? ss / (float)nw : 0.0f;
         float m2 = 0.0f;
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
                 }
             }
         }
-        m2 = wave_sum(m2);
+        m2 = row_sum(m2);
         mean = mw;
         if (WPR > 1) {
             if ((threadIdx.x & 63) == 0) moments[wave] = float4{ss, mw, m2, (float)nw};
@@ -207,6 +223,26 @@ void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, const IO
 #undef NRS_NORM
 }
 
+// Rows of at most 32 chunks: `seg` lanes per row, 256 / seg rows per block.
+template <typename IO, bool ADD, bool LN, bool NT>
+void launch_short(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, const IO *b, int64_t rows,
+                  int32_t nchunks, int seg, int64_t xs, int64_t ys, float inv_h, float eps,
+                  hipStream_t stream) {
+    const dim3 grid((unsigned)((rows + 256 / seg - 1) / (256 / seg))), block(256);
+#define NRS_SHORT(S)                                                                            \
+    hipLaunchKernelGGL((norm_kernel<IO, 1, 1, ADD, LN, NT, S>), grid, block, 0, stream, y, ro, x, \
+                       r, g, b, rows, nchunks, xs, ys, inv_h, eps)
+    switch (seg) {
+        case 1: NRS_SHORT(1); break;
+        case 2: NRS_SHORT(2); break;
+        case 4: NRS_SHORT(4); break;
+        case 8: NRS_SHORT(8); break;
+        case 16: NRS_SHORT(16); break;
+        default: NRS_SHORT(32); break;
+    }
+#undef NRS_SHORT
+}
+
 template <typename IO, bool ADD, bool LN>
 hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *res,
                              const void *gamma, const void *beta, int64_t rows, int64_t hidden,
@@ -220,6 +256,17 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma,
              *B = (const IO *)beta;
     const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
+    if (nchunks <= 32) {
+        int seg = 1;
+        while (seg < nchunks) seg <<= 1;
+        if (nt)
+            launch_short<IO, ADD, LN, true>(Y, RO, X, R, G, B, rows, nchunks, seg, x_stride,
+                                            y_stride, inv_h, eps, stream);
+        else
+            launch_short<IO, ADD, LN, false>(Y, RO, X, R, G, B, rows, nchunks, seg, x_stride,
+                                             y_stride, inv_h, eps, stream);
+        return hipGetLastError();
+    }
 #define NRS_SHAPE(W)                                                                             \
     (nt ? launch_shape<IO, ADD, LN, W, true>(Y, RO, X, R, G, B, rows, nchunks, nch, x_stride,      \
                                              y_stride, inv_h, eps, stream)                        \

@@ -186,6 +186,35 @@ def test_norm_widths(dt, hidden):
     check(f"width{hidden}/add.y", y, ry)
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("hidden", [16, 40, 128, 136, 256])
+@pytest.mark.parametrize("rows", [1, 37, 1000])
+def test_norm_short_rows_share_waves(dt, hidden, rows):
+    # rows of at most 32 chunks take an aligned lane group each, several per wave
+    if dt == torch.float32 and hidden == 136:
+        hidden = 132
+    x, r = _rand((rows, hidden), dt, 11), _rand((rows, hidden), dt, 12)
+    gamma = (1 + 0.1 * _rand((hidden,), torch.float32, 13)).to(dt)
+    y = nrs.rmsnorm(cuda(x), cuda(gamma), 1e-6)
+    check(f"short{hidden}x{rows}/rmsnorm", y, oracle.rmsnorm(x, gamma, f32(1e-6)))
+    y, ro = nrs.add_rmsnorm(cuda(x), cuda(r), cuda(gamma), 1e-6)
+    ry, rro = oracle.add_rmsnorm(x, r, gamma, f32(1e-6))
+    check_exact(f"short{hidden}x{rows}/add.residual_out", ro, rro)
+    check(f"short{hidden}x{rows}/add.y", y, ry)
+
+
+def test_per_head_norm_shape():
+    # a per-head RMSNorm over head_dim 128: 2048 tokens x 16 heads as 32768 rows of 128,
+    # strided inside a packed qkv row (token stride 32 heads x 128)
+    big = _rand((2048, 32 * 128), torch.bfloat16, 14)
+    q = cuda(big)[:, : 16 * 128].reshape(2048, 16, 128)
+    gamma = (1 + 0.1 * _rand((128,), torch.float32, 15)).to(torch.bfloat16)
+    y = nrs.rmsnorm(q.reshape(-1, 128) if q.is_contiguous() else q.contiguous().view(-1, 128),
+                    cuda(gamma), 1e-6)
+    ref = oracle.rmsnorm(big[:, : 16 * 128].reshape(-1, 128).contiguous(), gamma, f32(1e-6))
+    check("per_head128/rmsnorm", y, ref)
+
+
 @pytest.mark.parametrize("rows", [1, 3, 4, 5, 4095, 9000])
 def test_norm_row_counts(rows):
     x = _rand((rows, 2048), torch.bfloat16, rows)
