@@ -8,7 +8,9 @@ rmsnorm -> add_rmsnorm -> mrope (in place) -> swiglu, inputs resident in HBM.
 the same run times the decode-step op set (5 tokens x 28 layers of
 add_rmsnorm -> mrope -> swiglu, and the 4-op layer with the post-attention
 norm) replayed from one hipGraph, plus an empty-kernel graph with the same
-node count as the launch floor.
+node count as the launch floor.  `next_ops` times the ops built beside the
+step (LayerNorm, M-RoPE + KV-cache append, softmax + top-k sampling, and
+RMSNorm + Linear at the decode step's projection shapes and a prefill shape).
 
 Every duration is taken with HIP events recorded on the stream the kernels
 run on.  The oracle (the fp64 C reference) is timed on a bounded sample of the

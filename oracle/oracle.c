@@ -1,5 +1,8 @@
 /*
- * fp64 CPU oracle for the four per-token decoder-layer ops.
+ * fp64 CPU oracle for the per-token decoder-layer ops (RMSNorm, the fused
+ * residual add + RMSNorm, M-RoPE, SwiGLU) and the ops built beside them
+ * (M-RoPE + KV-cache append, softmax + top-k sampling, LayerNorm, RMSNorm +
+ * Linear).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
