@@ -87,16 +87,29 @@ def cpu_baseline(w, n_tokens):
     x, res, gamma = L.x[sl].cpu(), L.residual[sl].cpu(), L.gamma.cpu()
     q, k, gu, pos = L.q[sl].cpu(), L.k[sl].cpu(), L.gate_up[sl].cpu(), w.pos[:, sl].cpu().contiguous()
     eps = float(np.float32(w.eps))
-    t0 = time.perf_counter()
-    oracle.rmsnorm(x, gamma, eps)
-    oracle.add_rmsnorm(x, res, gamma, eps)
-    oracle.mrope(q, k, pos, w.sections, w.theta)
-    oracle.swiglu(gu)
-    dt = time.perf_counter() - t0
+    per_op_ms = {}
+    t_all = time.perf_counter()
+    for op, fn in (("rmsnorm", lambda: oracle.rmsnorm(x, gamma, eps)),
+                   ("add_rmsnorm", lambda: oracle.add_rmsnorm(x, res, gamma, eps)),
+                   ("mrope", lambda: oracle.mrope(q, k, pos, w.sections, w.theta)),
+                   ("swiglu", lambda: oracle.swiglu(gu))):
+        t0 = time.perf_counter()
+        fn()
+        per_op_ms[op] = round(1e3 * (time.perf_counter() - t0), 1)
+    dt = time.perf_counter() - t_all
     byts = sum(algorithmic_bytes(op, n_tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2)
                for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu"))
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(byts / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "per_op_ms": per_op_ms, "host_cpu": cpu,
+            "host_threads_available": os.cpu_count(),
             "sample": f"first {n_tokens} of {w.tokens} tokens of the step's batch, all four ops, "
                       "fp64 C oracle on one host thread, same algorithmic-byte count"}
 
