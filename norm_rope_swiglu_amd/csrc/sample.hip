@@ -13,12 +13,14 @@
 //
 // One 1024-thread workgroup per row:
 //   1. radix select of the k-th largest logit on monotone 32-bit keys, 8 bits
-//      per pass (4 passes for fp32, 2 for bf16, whose low 16 key bits are
-//      fixed by the sign), histograms in LDS;
-//   2. one pass gathers every logit above that key and every tie at it (the
-//      histogram counts them) when they fit the 1024-entry buffer; only
-//      longer tie runs take an ordered compaction (a block-wide prefix count
-//      per 1024 chunks keeps the lowest-index ties);
+//      per pass for register-held rows and 12 for streamed ones (bf16 keys
+//      vary in 16 bits, fp32 in 32), histograms in LDS, stopping as soon as
+//      everything above the selected bin plus the bin fits the 1024-entry
+//      gather buffer;
+//   2. one pass gathers every logit in or above the selected bin (the
+//      histogram counts them) when they fit; only tie runs longer than the
+//      buffer take an ordered compaction (a block-wide prefix count per 1024
+//      chunks keeps the lowest-index ties);
 //   3. a sort of the gathered entries by (logit descending, index ascending):
 //      lane exchanges within one wave for up to 64, a bitonic network in LDS
 //      beyond;
@@ -38,6 +40,12 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;  // chunks in flight per thread in the passes over the row
+// Radix digit and histogram replicas: rows streamed from memory take 12-bit
+// digits (4096 bins, 4 replicas), so the first pass usually narrows the
+// candidates enough to skip the rest and one read of the row is saved;
+// register-held rows take 8-bit digits (256 bins, 32 replicas), whose smaller
+// histograms cost less to clear and scan than an extra pass over registers.
+constexpr int kHistWords = 16384;
 
 // Order-preserving map of an fp32 value to uint32 (larger value, larger key);
 // -0 is folded onto +0 so equal values have equal keys.
@@ -137,8 +145,11 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     using K = keys<IO>;
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    constexpr int NPASS = sizeof(IO) == 4 ? 4 : 2;
-    __shared__ uint32_t hist[256 * 32];   // 256 digits x 32 bank replicas
+    constexpr int kDigitBits = CPT > 0 ? 8 : 12;
+    constexpr int kRep = CPT > 0 ? 32 : 4;
+    static_assert((kRep << kDigitBits) <= kHistWords, "histogram fits");
+    // bin-major: the replicas of a bin sit on kRep consecutive banks
+    __shared__ uint32_t hist[kHistWords];
     __shared__ uint32_t wtot[4];
     __shared__ uint32_t sel[3];            // selected digit, count above it, count equal
     __shared__ int iscan[kWaves];
@@ -202,15 +213,29 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         }
     };
 
-    // 1. radix select: find the top_k-th largest key.  Each bin is replicated
-    //    across the 32 LDS banks (indexed by lane) so lanes counting the same
-    //    digit, common with peaky logits, rarely hit one address.
+    // 1. radix select: find the top_k-th largest key, kDigitBits at a time from
+    //    the top (streamed bf16 keys: 12 + 4 bits; fp32: 12 + 12 + 8).  The
+    //    remaining digits are left to the sort once every key above the
+    //    selected bin plus the bin itself fits one wave (64), or, for a
+    //    streamed row, the 1024-entry gather buffer (with 12-bit digits this
+    //    usually happens after the first pass, so a streamed row is read twice:
+    //    once counted, once gathered).  The
+    //    histograms keep replicas (indexed by lane) so lanes counting the same
+    //    bin, common with peaky logits, split over several addresses.
+    constexpr int kKeyBits = sizeof(IO) == 4 ? 32 : 16;   // bits that vary in a key
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)top_k;
-    const uint32_t rep = tid & 31;
-    for (int pass = 0; pass < NPASS; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256 * 32; i += kThreads) hist[i] = 0;
+    const uint32_t rep = tid & (kRep - 1);
+    bool fits = false;
+    constexpr int kPasses = (kKeyBits + kDigitBits - 1) / kDigitBits;
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        // digit bits [shift, top): constants once the loop is unrolled
+        const int top = 32 - pass * kDigitBits;
+        const int bits = top - (32 - kKeyBits) < kDigitBits ? top - (32 - kKeyBits) : kDigitBits;
+        const int shift = top - bits;
+        const uint32_t nb = 1u << bits;
+        for (int i = tid; i < (int)nb * kRep; i += kThreads) hist[i] = 0;
         opaque();
         __syncthreads();
         for_chunks([&](int64_t, const u32x4 &kc) {
@@ -218,48 +243,90 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
             for (int e = 0; e < VEC; ++e) {
                 const uint32_t key = K::at(kc, e);
                 if ((key & pmask) == prefix)
-                    atomicAdd(&hist[((key >> shift) & 255u) * 32 + rep], 1u);
+                    atomicAdd(&hist[((key >> shift) & (nb - 1)) * kRep + rep], 1u);
             }
         });
         __syncthreads();
-        // thread t < 256 sums digit 255 - t (rotating the replica index keeps
-        // the 64 lanes of a wave on different banks); an inclusive scan over t
-        // then counts the candidates with digit >= 255 - t: per wave first,
-        // then, after a barrier every thread reaches, across the four waves
-        const uint32_t d = 255u - (uint32_t)(tid & 255);
-        uint32_t h = 0, incl = 0;
-        if (tid < 256) {
-            for (int r = 0; r < 32; ++r) h += hist[d * 32 + ((r + tid) & 31)];
-            incl = h;
-            const int lane = tid & 63;
+        if (nb <= 256) {
+            // thread t < nb sums digit nb-1-t (rotating the replica index keeps
+            // a wave's lanes on different banks); an inclusive scan over t then
+            // counts the candidates with digit >= nb-1-t: per wave first, then,
+            // after a barrier every thread reaches, across the (at most four) waves
+            const uint32_t d = nb - 1 - (uint32_t)(tid & 255);
+            uint32_t h = 0, incl = 0;
+            if (tid < (int)nb) {
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t up = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += up;
+                for (int r = 0; r < kRep; ++r) h += hist[d * kRep + ((r + tid) & (kRep - 1))];
+                incl = h;
+                const int lane = tid & 63;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t up = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += up;
+                }
+                if (lane == 63) wtot[tid >> 6] = incl;
             }
-            if (lane == 63) wtot[tid >> 6] = incl;
-        }
-        __syncthreads();
-        if (tid < 256) {
-            for (int w2 = 0; w2 < (tid >> 6); ++w2) incl += wtot[w2];
-            if (incl - h < need && need <= incl) {  // the need-th largest has digit d
-                sel[0] = d;
-                sel[1] = incl - h;
-                sel[2] = h;
+            __syncthreads();
+            if (tid < (int)nb) {
+                for (int w2 = 0; w2 < (tid >> 6); ++w2) incl += wtot[w2];
+                if (incl - h < need && need <= incl) {   // the need-th largest has digit d
+                    sel[0] = d;
+                    sel[1] = incl - h;
+                    sel[2] = h;
+                }
+            }
+        } else {
+            // thread t sums bins nb-1-t*bpt .. nb-bpt-t*bpt (largest digits
+            // first); a block scan finds the thread whose bins hold the need-th
+            // largest key, which then walks its bins
+            const int bpt = (int)nb / kThreads;
+            uint32_t hsum = 0;
+            for (int j = 0; j < bpt; ++j) {
+                const uint32_t d = nb - 1 - (uint32_t)(tid * bpt + j);
+#pragma unroll
+                for (int r = 0; r < kRep; ++r) hsum += hist[d * kRep + ((r + tid) & (kRep - 1))];
+            }
+            int total;
+            const uint32_t before = (uint32_t)block_exclusive_scan((int)hsum, iscan, total);
+            if (before < need && need <= before + hsum) {
+                uint32_t above = before;
+                for (int j = 0; j < bpt; ++j) {
+                    const uint32_t d = nb - 1 - (uint32_t)(tid * bpt + j);
+                    uint32_t h = 0;
+#pragma unroll
+                    for (int r = 0; r < kRep; ++r) h += hist[d * kRep + r];
+                    if (above < need && need <= above + h) {
+                        sel[0] = d;
+                        sel[1] = above;
+                        sel[2] = h;
+                        break;
+                    }
+                    above += h;
+                }
             }
         }
         __syncthreads();
         prefix |= sel[0] << shift;
-        pmask |= 255u << shift;
+        pmask |= (nb - 1) << shift;
         need -= sel[1];
-        __syncthreads();
+        // the candidates left (the same in every thread): stop early when one
+        // wave can sort them, or, for a streamed row, when they fit the buffer
+        // (a read of the row saved outweighs the larger sort); after the last
+        // digit, whenever they fit the buffer
+        const int cand = (top_k - (int)need) + (int)sel[2];
+        const bool last = shift == 32 - kKeyBits;
+        fits = cand <= kThreads;
+        const bool stop = last || cand <= 64 || (CPT == 0 && fits);
+        __syncthreads();                                        // sel is rewritten next pass
+        if (stop) break;
     }
-    // keys below the selected passes are fixed (bf16: the low 16 bits follow
-    // the sign), so one representative key decides the comparisons
+    // keys below the selected digits are either left to the sort (fits) or
+    // fixed (bf16: the low 16 bits follow the sign), so one representative
+    // key decides the comparisons
     const uint32_t kth = prefix;
     const uint32_t kth_mask = pmask;
     const int n_above = top_k - (int)need;   // keys strictly above kth
-    const int n_tied = (int)sel[2];          // keys equal to kth (the last pass's bin)
+    const int n_tied = (int)sel[2];          // keys equal to kth under kth_mask
 
     // 2. gather the kept entries.  When everything above kth and every tie at
     //    kth fits the 1024-entry buffer, one pass appends them all in any
@@ -267,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     //    ordered compaction keeps exactly the lowest-index `need` ties.
     if (tid == 0) n_gt = 0;
     __syncthreads();
-    const bool gather_all = n_above + n_tied <= kThreads;
+    const bool gather_all = fits;
     const int n_kept = gather_all ? n_above + n_tied : top_k;   // entries to sort
     if (gather_all) {
         opaque();
