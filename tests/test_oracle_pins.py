@@ -10,6 +10,7 @@ from __future__ import annotations
 import json
 import math
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -19,6 +20,14 @@ import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 rng = np.random.default_rng(12345)
+
+
+@pytest.fixture(autouse=True)
+def _rng_per_test(request):
+    """Each test draws from its own generator, seeded by its id, so its inputs
+    do not depend on which tests ran before it (or on which worker)."""
+    global rng
+    rng = np.random.default_rng(zlib.crc32(request.node.nodeid.encode()))
 
 
 def t32(a):
@@ -361,8 +370,12 @@ def test_mrope_equal_streams_is_complex_rope(D, sections):
     for v, out in ((q, qo), (k, ko)):
         z = v.double().numpy()
         zc = (z[..., :half] + 1j * z[..., half:]) * rot
-        np.testing.assert_allclose(out[..., :half], zc.real, rtol=0, atol=1e-11)
-        np.testing.assert_allclose(out[..., half:], zc.imag, rtol=0, atol=1e-11)
+        # two fp64 evaluations of the angle p * theta^(-2j/D) (C pow vs numpy's)
+        # may differ by a few ulps of p: the rotated pair then moves by up to
+        # |pair| * p * 2^-52 * a few
+        tol = 8 * 2.0**-52 * float(p.max()) * float(np.abs(z).max()) * math.sqrt(2) + 1e-15
+        np.testing.assert_allclose(out[..., :half], zc.real, rtol=0, atol=tol)
+        np.testing.assert_allclose(out[..., half:], zc.imag, rtol=0, atol=tol)
 
 
 def test_mrope_frequency_schedule():
