@@ -1,7 +1,6 @@
 // C-ABI entry points of libnrs: validate on the host, then enqueue.
 // The declarations, with argument meaning and error behaviour, are in nrs.h.
 #include <math.h>
-#include <stdio.h>
 
 #include <new>
 

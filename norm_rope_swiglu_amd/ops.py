@@ -361,6 +361,8 @@ def decode_graph(layers: list[dict], pos: torch.Tensor, sections, theta: float, 
             t = L.get(key)
             if t is None:
                 continue
+            if t.dtype != L0["in_x"].dtype or t.device != L0["in_x"].device:
+                raise TypeError(f"layer {i} {key}: every tensor must share in_x's dtype and device")
             if not t.is_contiguous():
                 raise ValueError(f"layer {i} {key} must be contiguous")
             keep.append(t)
