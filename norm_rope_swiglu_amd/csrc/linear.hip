@@ -24,11 +24,13 @@
 // to 10% slower.
 //
 // With many rows (bf16) it is a GEMM bound by the matrix cores: 256 x 256
-// output tiles of eight waves of 64 x 128 each when the problem has enough of
-// them to fill the chip, 128 x 128 tiles of four 64 x 64 waves otherwise,
-// operands staged through
-// double-buffered, swizzled LDS 64 inputs at a time, and the row sums of squares taken
-// from the A fragments as the tiles stream through.
+// output tiles when the problem has enough of them to fill the chip, else
+// 256 x 128; eight waves per tile in two groups that take turns between
+// multiplying and reading LDS; operands loaded straight into a three-slot LDS
+// ring; the row sums of squares taken from the A fragments as the tiles
+// stream through (details above the kernel).
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -38,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // One step of a 16x16 output tile over 4 * VEC inputs.  Lane (r, g) = (lane %
 // 16, lane / 16) supplies a 16-byte chunk of A row r and of B column r, both
@@ -162,132 +165,239 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
 }
 
 // ---------------------------------------------------------------- many rows (GEMM)
+//
+// A 256-row tile of x against BN weight rows, BK inputs per stage, eight
+// waves in two groups of four.  Group h owns tile rows [128 h, 128 h + 128);
+// its waves split them 2 x 2, so each wave holds a 64 x BN/2 block of 16 x 16
+// accumulators.  Each SIMD runs one wave of each group, and the groups take
+// turns: while one multiplies the stage it holds in registers, the other
+// reads its next stage's fragments from LDS and issues the loads of a later
+// stage, and one workgroup barrier separates the turns.  Measured on MI355X,
+// a wave reads LDS at ~40 B/clk on its own and the CU at ~240 B/clk with
+// eight waves, while 16-byte LDS stores peak at ~78 B/clk.  So the operands
+// reach LDS by buffer loads that write LDS directly (no register staging and
+// no LDS store instructions), into a ring of three stage slots held as
+// separate arrays.  The compiler then orders each fragment read only after
+// the loads into its own slot.
 
-constexpr int kGBK = 64;                // inputs per LDS stage: one 128-byte LDS row per tile row
+// 16-byte chunk c of tile row `row` in a stage slot whose rows are CPR chunks
+// long: the chunk is stored at slot c ^ swizzle(row), which spreads both a
+// fragment read (16 consecutive rows, one chunk) and a 1 KiB load over every
+// bank.
+template <int CPR> __device__ inline int gemm_swizzle(int row) {
+    if constexpr (CPR == 8) return (row >> 1) & 7;
+    else return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+}
+template <int CPR> __device__ inline int gemm_at(int row, int c) {
+    return row * CPR * 8 + ((c ^ gemm_swizzle<CPR>(row)) << 3);
+}
 
-// LDS element offset of 16-byte chunk c (0..7) of tile row `row`.  The chunk's
-// slot is XOR-swizzled by bits 1..3 of the row, so both access patterns fill
-// all 64 banks once per 16 lanes: a fragment load (16 consecutive rows, one
-// chunk) and a staging store (two rows, all eight chunks).  Against 144-byte
-// padded rows it removes the staging stores' bank conflicts and 18 KiB of
-// LDS; measured speed is the same to within run-to-run spread.
-__device__ inline int lds_at(int row, int c) { return row * kGBK + ((c ^ ((row >> 1) & 7)) << 3); }
+// s_waitcnt with vmcnt = N and the other counters at their maximum
+template <int N> __device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
-// One workgroup of WM x WN waves computes a (16 WM TM) x (16 WN TN) tile of
-// out; wave (wm, wn) owns TM x TN MFMA tiles of 16 x 16, so every 16-byte
-// fragment read from LDS feeds TN (A) or TM (B) matrix-core steps.  Each
-// stage every thread moves 16-byte chunks of x and w from HBM into registers
-// while the waves multiply the stage already in LDS; then it writes them to
-// the other LDS buffer and all meet at one barrier.
-template <int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(64 * WM * WN) void rmsnorm_linear_gemm_kernel(
+// a workgroup barrier that waits for nothing itself (the waits before it are
+// explicit), and that the compiler does not move memory accesses across
+__device__ inline void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// one 16-byte load per lane from buffer r at voff + soff, lane l writing
+// bytes [16 l, 16 l + 16) after lds (wave-uniform)
+__device__ inline void load_to_lds(__amdgpu_buffer_rsrc_t r, __bf16 *lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+constexpr int kGemmRows = 256;           // x rows per tile
+constexpr int kGemmGroupRows = 4;        // row tiles per group of the tile order
+
+template <int BN, int BK>
+__global__ __launch_bounds__(512, 1) void rmsnorm_linear_gemm_kernel(
     __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t rows, int32_t n_in, int64_t n_out,
     int64_t x_stride, int64_t w_stride, int64_t out_stride, float inv_n, float eps,
     uint32_t mblocks, uint32_t nblocks) {
-    constexpr int kGBM = 16 * WM * TM, kGBN = 16 * WN * TN;
-    constexpr int kGThreads = 64 * WM * WN;
-    constexpr int kGTM = TM, kGTN = TN;
-    static_assert(kGBM == kGBN, "one staging map serves both operands");
-    constexpr int kGChunks = kGBM * kGBK / 8 / kGThreads;   // 16-byte chunks per thread per operand
-    __shared__ __attribute__((aligned(16))) __bf16 As[2][kGBM * kGBK];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kGBN * kGBK];
-    __shared__ float row_ss[kGBM];
+    constexpr int BM = kGemmRows, TM = 4, TN = BN / 32, KS = BK / 32, CPR = BK / 8;
+    constexpr int RPK = 64 / CPR;                         // tile rows per 1 KiB load
+    constexpr int NA = (BM / 2) / RPK / 4, NB = (BN / 2) / RPK / 4;   // loads per wave per stage
+    constexpr int NL = NA + NB;
+    static_assert(NA * RPK * 4 == BM / 2 && NB * RPK * 4 == BN / 2, "loads split evenly");
+    constexpr int D = 2;                                  // stages in flight ahead of the one read
+    __shared__ __attribute__((aligned(16))) __bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK];
+    __shared__ __attribute__((aligned(16))) __bf16 B0[BN * BK], B1[BN * BK], B2[BN * BK];
+    __shared__ float row_ss[BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
+    const int grp = wave >> 2, wig = wave & 3, wm = wig >> 1, wn = wig & 1;
     const int r = lane & 15, g = lane >> 4;
-    const int wm = wave / WN, wn = wave % WN;
-    // consecutive tiles of one XCD share a weight tile and walk down the rows
+    // each XCD runs consecutive tiles together; they are taken in groups of
+    // kGemmGroupRows row tiles across all column tiles, so the tiles in
+    // flight on one XCD share row and column tiles in its L2
+    constexpr uint32_t GM = kGemmGroupRows;
     const uint32_t b = xcd_contiguous(blockIdx.x, mblocks * nblocks);
-    const int64_t m0 = (int64_t)(b % mblocks) * kGBM, c0 = (int64_t)(b / mblocks) * kGBN;
-    const int nstages = (n_in + kGBK - 1) / kGBK;
-    const u32x4 zero = {0, 0, 0, 0};
+    const uint32_t gid = b / (GM * nblocks), first = gid * GM;
+    const uint32_t gsz = mblocks - first < GM ? mblocks - first : GM;
+    const uint32_t within = b - gid * GM * nblocks;
+    const int64_t m0 = (int64_t)(first + within % gsz) * BM, c0 = (int64_t)(within / gsz) * BN;
+    const int nst = (n_in + BK - 1) / BK;
 
-    // staging map: chunk q = tid + threads * j is row q / 8, inputs 8 (q % 8) .. + 7
-    u32x4 ra[kGChunks], rb[kGChunks];
-    auto gload = [&](int st) {
-#pragma unroll
-        for (int j = 0; j < kGChunks; ++j) {
-            const int q = tid + kGThreads * j, row = q >> 3, n = st * kGBK + (q & 7) * 8;
-            const bool nin = n < n_in;                      // n_in is whole chunks
-            ra[j] = nin && m0 + row < rows ? load16(x + (m0 + row) * x_stride + n) : zero;
-            rb[j] = nin && c0 + row < n_out ? load16(w + (c0 + row) * w_stride + n) : zero;
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < kGChunks; ++j) {
-            const int q = tid + kGThreads * j, at = lds_at(q >> 3, q & 7);
-            *reinterpret_cast<u32x4 *>(&As[buf][at]) = ra[j];
-            *reinterpret_cast<u32x4 *>(&Bs[buf][at]) = rb[j];
-        }
-    };
+    // buffers based at the tile's first row and covering only its rows inside
+    // the matrix, so loads of rows past the end read zeros
+    const int a_rows = (int)(rows - m0 < BM ? rows - m0 : BM);
+    const int b_rows = (int)(n_out - c0 < BN ? n_out - c0 : BN);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + m0 * x_stride), 0, (int)((int64_t)a_rows * x_stride * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(w + c0 * w_stride), 0, (int)((int64_t)b_rows * w_stride * 2), 0x00020000);
+    constexpr uint32_t kOut = 0x80000000u;    // beyond any buffer here: reads as zeros
 
-    f32x4 acc[kGTM][kGTN];
-    float ssq[kGTM];
+    // this wave's loads.  Load j covers RPK tile rows; lane l fills LDS slot l
+    // of that 1 KiB block, i.e. row base + l / CPR, stored chunk l % CPR,
+    // which holds input chunk (l % CPR) ^ swizzle(row).
+    uint32_t offa[NA], offb[NB];
+    int cla[NA], clb[NB];
 #pragma unroll
-    for (int i = 0; i < kGTM; ++i) {
-        ssq[i] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kGTN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NA; ++j) {
+        const int lr = grp * (BM / 2) + (wig * NA + j) * RPK + lane / CPR;
+        cla[j] = ((lane % CPR) ^ gemm_swizzle<CPR>(lr)) * 8;
+        offa[j] = (uint32_t)(lr * (int)x_stride + cla[j]) * 2u;
     }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int lr = grp * (BN / 2) + (wig * NB + j) * RPK + lane / CPR;
+        clb[j] = ((lane % CPR) ^ gemm_swizzle<CPR>(lr)) * 8;
+        offb[j] = (uint32_t)(lr * (int)w_stride + clb[j]) * 2u;
+    }
+    // stage st of this wave's share into a slot; only the last stage can
+    // reach past n_in, and its lanes beyond it read zeros
+    auto issue = [&](auto steady, int st, auto &As, auto &Bs) {
+        const int k0 = st * BK;
+        const bool tail = !decltype(steady)::value && k0 + BK > n_in;
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+            load_to_lds(ar, &As[(grp * (BM / 2) + (wig * NA + j) * RPK) * BK],
+                        tail && k0 + cla[j] >= n_in ? kOut : offa[j], k0 * 2);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            load_to_lds(br, &Bs[(grp * (BN / 2) + (wig * NB + j) * RPK) * BK],
+                        tail && k0 + clb[j] >= n_in ? kOut : offb[j], k0 * 2);
+    };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int st = 0; st < nstages; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstages) gload(st + 1);
+    f32x4 acc[TM][TN];
+    float ssq0 = 0.0f, ssq1 = 0.0f;     // sums of squares of rows t = 2 wn, 2 wn + 1
 #pragma unroll
-        for (int kk = 0; kk < kGBK; kk += 32) {
-            u32x4 af[kGTM], bf[kGTN];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int t = 0; t < kGTM; ++t)
-                af[t] = *reinterpret_cast<const u32x4 *>(
-                    &As[buf][lds_at(wm * 16 * kGTM + t * 16 + r, (kk >> 3) + g)]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int arow = grp * (BM / 2) + wm * 64 + r, brow = wn * (BN / 2) + r;
+
+    // one stage: the fragment turn, a barrier, the multiply turn, a barrier
+    auto body = [&](auto steady, int st, const auto &As, const auto &Bs, auto &An, auto &Bn) {
+        u32x4 af[KS][TM], bf[KS][TN];
 #pragma unroll
-            for (int t = 0; t < kGTN; ++t)
-                bf[t] = *reinterpret_cast<const u32x4 *>(
-                    &Bs[buf][lds_at(wn * 16 * kGTN + t * 16 + r, (kk >> 3) + g)]);
-            if (wn == 0) {   // one wave per row band takes the rows' sums of squares
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int t = 0; t < kGTM; ++t) {
-                    float v[8];
-                    io_traits<__bf16>::unpack(af[t], v);
+            for (int t = 0; t < TM; ++t)
+                af[ks][t] = *reinterpret_cast<const u32x4 *>(&As[gemm_at<CPR>(arow + t * 16, ks * 4 + g)]);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) ssq[t] = __builtin_fmaf(v[i], v[i], ssq[t]);
+            for (int t = 0; t < TN; ++t)
+                bf[ks][t] = *reinterpret_cast<const u32x4 *>(&Bs[gemm_at<CPR>(brow + t * 16, ks * 4 + g)]);
+        }
+        // stage st + D into the slot stage st - 1 used, which every wave has
+        // finished reading (its reads completed before the last barrier)
+        const bool more = decltype(steady)::value || st + D < nst;
+        if (more) issue(steady, st + D, An, Bn);
+        wait_lgkmcnt0();
+        // this wave's share of stage st + 1 must have landed before the
+        // barrier after which the other group reads it
+        if (more) wait_vmcnt<(D - 1) * NL>();
+        else wait_vmcnt<0>();
+        bare_barrier();
+        // the fragments pass through an empty asm so that no multiply is
+        // hoisted above the barrier
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(af[ks][t]));
+#pragma unroll
+            for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(bf[ks][t]));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            {   // sums of squares: the two waves of a row band take two A fragments each
+                const u32x4 a0 = wn ? af[ks][2] : af[ks][0], a1 = wn ? af[ks][3] : af[ks][1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ssq0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (unsigned)a0[i]),
+                                                           __builtin_bit_cast(bf16x2, (unsigned)a0[i]), ssq0, false);
+                    ssq1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (unsigned)a1[i]),
+                                                           __builtin_bit_cast(bf16x2, (unsigned)a1[i]), ssq1, false);
                 }
             }
 #pragma unroll
-            for (int tm = 0; tm < kGTM; ++tm)
+            for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < kGTN; ++tn)
-                    acc[tm][tn] = mfma_step<__bf16>::run(af[tm], bf[tn], acc[tm][tn]);
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = mfma_step<__bf16>::run(af[ks][tm], bf[ks][tn], acc[tm][tn]);
         }
-        if (st + 1 < nstages) lstore(buf ^ 1);
-        __syncthreads();
-    }
+        __builtin_amdgcn_sched_barrier(0);
+        bare_barrier();
+    };
 
-    if (wn == 0) {
-#pragma unroll
-        for (int t = 0; t < kGTM; ++t) {
-            float s2 = ssq[t];
-            s2 += __shfl_xor(s2, 16);
-            s2 += __shfl_xor(s2, 32);
-            if (g == 0) row_ss[wm * 16 * kGTM + t * 16 + r] = s2;
-        }
+    // prologue: stages 0 and 1 in flight, stage 0 landed and visible; then
+    // group 1 passes one extra barrier so the groups run a turn apart
+    issue(std::false_type{}, 0, A0, B0);
+    if (nst > 1) issue(std::false_type{}, 1, A1, B1);
+    if (nst > 1) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    bare_barrier();
+    if (grp) bare_barrier();
+    // steady state: every stage loads the one D ahead, with no branches
+    // between the ring's slots (a branch there would cost the compiler its
+    // per-slot ordering of loads and reads); every stage it loads lies wholly
+    // inside n_in
+    const int nfull = n_in / BK;
+    int st = 0;
+    for (; st + 3 + D <= nfull; st += 3) {
+        body(std::true_type{}, st, A0, B0, A2, B2);
+        body(std::true_type{}, st + 1, A1, B1, A0, B0);
+        body(std::true_type{}, st + 2, A2, B2, A1, B1);
+    }
+    for (; st < nst; st += 3) {
+        body(std::false_type{}, st, A0, B0, A2, B2);
+        if (st + 1 < nst) body(std::false_type{}, st + 1, A1, B1, A0, B0);
+        if (st + 2 < nst) body(std::false_type{}, st + 2, A2, B2, A1, B1);
+    }
+    if (!grp) bare_barrier();    // both groups have now passed the same number
+
+    // sums of squares over the four lane groups, then one row each in LDS
+    ssq0 += __shfl_xor(ssq0, 16);
+    ssq0 += __shfl_xor(ssq0, 32);
+    ssq1 += __shfl_xor(ssq1, 16);
+    ssq1 += __shfl_xor(ssq1, 32);
+    if (g == 0) {
+        row_ss[arow + 2 * wn * 16] = ssq0;
+        row_ss[arow + (2 * wn + 1) * 16] = ssq1;
     }
     __syncthreads();
 #pragma unroll
-    for (int tm = 0; tm < kGTM; ++tm) {
+    for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = wm * 16 * kGTM + tm * 16 + 4 * g + i;   // accumulator layout
+            const int row = grp * (BM / 2) + wm * 64 + tm * 16 + 4 * g + i;   // accumulator layout
             const int64_t gm = m0 + row;
             if (gm >= rows) continue;
             const float rs = rsqrtf(__builtin_fmaf(row_ss[row], inv_n, eps));
 #pragma unroll
-            for (int tn = 0; tn < kGTN; ++tn) {
-                const int64_t gc = c0 + wn * 16 * kGTN + tn * 16 + r;
+            for (int tn = 0; tn < TN; ++tn) {
+                const int64_t gc = c0 + wn * (BN / 2) + tn * 16 + r;
                 if (gc < n_out) out[gm * out_stride + gc] = (__bf16)(acc[tm][tn][i] * rs);
             }
         }
@@ -298,6 +408,8 @@ namespace {
 
 constexpr int kSplit = 8;      // waves per workgroup (splitting the input dimension)
 constexpr int kMaxTileRows = 64;
+// the tiled path addresses a tile's rows with 32-bit byte offsets
+constexpr int64_t kMaxGemmStride = (int64_t)1 << 22;
 
 template <typename IO>
 void launch_chunk(IO *out, const IO *x, const IO *w, int32_t rows, int32_t n_in, int64_t n_out,
@@ -312,38 +424,42 @@ void launch_chunk(IO *out, const IO *x, const IO *w, int32_t rows, int32_t n_in,
 #undef NRS_LIN
 }
 
+// bf16, many rows: 256 x 256 tiles (32 inputs per stage) when they give every
+// CU one, else 256 x 128 (64 inputs per stage)
+hipError_t launch_gemm(void *out, const void *x, const void *w, int64_t rows, int64_t n_in,
+                       int64_t n_out, int64_t xs, int64_t ws, int64_t os, float inv_n, float eps,
+                       hipStream_t stream) {
+    const int64_t big = ((rows + kGemmRows - 1) / kGemmRows) * ((n_out + 255) / 256);
+    const int tile = big >= 256 ? 256 : 128;
+    const uint32_t nblocks = (uint32_t)((n_out + tile - 1) / tile);
+    // rows per launch: whole tiles, and a grid below 2^31 workgroups
+    const int64_t max_mblocks = (((int64_t)1 << 31) - 1) / nblocks;
+    for (int64_t r0 = 0; r0 < rows; r0 += max_mblocks * kGemmRows) {
+        const int64_t rr = rows - r0 < max_mblocks * kGemmRows ? rows - r0 : max_mblocks * kGemmRows;
+        const uint32_t mblocks = (uint32_t)((rr + kGemmRows - 1) / kGemmRows);
+        __bf16 *o = (__bf16 *)out + r0 * os;
+        const __bf16 *xx = (const __bf16 *)x + r0 * xs;
+        if (tile == 256)
+            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<256, 32>), dim3(mblocks * nblocks), dim3(512),
+                               0, stream, o, xx, (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out,
+                               xs, ws, os, inv_n, eps, mblocks, nblocks);
+        else
+            hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<128, 64>), dim3(mblocks * nblocks), dim3(512),
+                               0, stream, o, xx, (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out,
+                               xs, ws, os, inv_n, eps, mblocks, nblocks);
+    }
+    return hipGetLastError();
+}
+
 template <typename IO>
 hipError_t launch_typed(void *out, const void *x, const void *w, int64_t rows, int64_t n_in,
                         int64_t n_out, int64_t xs, int64_t ws, int64_t os, float eps,
                         hipStream_t stream) {
     const float inv_n = (float)(1.0 / (double)n_in);
-    if (sizeof(IO) == 2 && rows > kMaxTileRows) {
-        // 256 x 256 tiles read half the operand bytes per flop of 128 x 128
-        // ones but need enough of them to give every CU one
-        const int64_t big = ((rows + 255) / 256) * ((n_out + 255) / 256);
-        const int tile = big >= 256 ? 256 : 128;
-        const uint32_t nblocks = (uint32_t)((n_out + tile - 1) / tile);
-        // rows per launch: whole tiles, and a grid below 2^31 workgroups
-        const int64_t max_mblocks = (((int64_t)1 << 31) - 1) / nblocks;
-        for (int64_t r0 = 0; r0 < rows; r0 += max_mblocks * tile) {
-            const int64_t rr = rows - r0 < max_mblocks * tile ? rows - r0 : max_mblocks * tile;
-            const uint32_t mblocks = (uint32_t)((rr + tile - 1) / tile);
-            __bf16 *o = (__bf16 *)out + r0 * os;
-            const __bf16 *xx = (const __bf16 *)x + r0 * xs;
-            if (tile == 256)
-                hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<4, 2, 4, 8>),
-                                   dim3(mblocks * nblocks), dim3(512), 0, stream, o, xx,
-                                   (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out, xs, ws,
-                                   os, inv_n, eps, mblocks, nblocks);
-            else
-                hipLaunchKernelGGL((rmsnorm_linear_gemm_kernel<2, 2, 4, 4>),
-                                   dim3(mblocks * nblocks), dim3(256), 0, stream, o, xx,
-                                   (const __bf16 *)w, (int32_t)rr, (int32_t)n_in, n_out, xs, ws,
-                                   os, inv_n, eps, mblocks, nblocks);
-        }
-        return hipGetLastError();
-    }
-    // fp32 rows beyond one launch's 64 are taken 64 at a time (each pass streams w again)
+    if (sizeof(IO) == 2 && rows > kMaxTileRows && xs < kMaxGemmStride && ws < kMaxGemmStride)
+        return launch_gemm(out, x, w, rows, n_in, n_out, xs, ws, os, inv_n, eps, stream);
+    // fp32 rows (and bf16 rows of very long strides) beyond one launch's 64
+    // are taken 64 at a time (each pass streams w again)
     for (int64_t m0 = 0; m0 < rows; m0 += kMaxTileRows) {
         const int32_t mr = (int32_t)(rows - m0 < kMaxTileRows ? rows - m0 : kMaxTileRows);
         IO *o = (IO *)out + m0 * os;

@@ -163,3 +163,20 @@ def test_fp32_many_rows_in_64_row_passes():
     # fp32 rows beyond 64 go through the few-row kernel 64 rows at a time
     x, w = lin_inputs(150, 512, 80, "f32", 14)
     lin_parity(x, w, 1e-6, "lin/f32/rows150")
+
+
+def test_gemm_long_row_stride():
+    # rows 2^22 elements apart exceed the tiled path's 32-bit tile offsets and
+    # take the 64-row passes instead; both must agree with the oracle
+    x, w = lin_inputs(66, 64, 40, "bf16", 15)
+    stride = 1 << 22
+    big = torch.zeros(66 * stride, dtype=torch.bfloat16, device="cuda")
+    xs = big.as_strided((66, 64), (stride, 1))
+    xs.copy_(x.cuda())
+    y = nrs.rmsnorm_linear(xs, w.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_linear(x, w, _f32(1e-6))
+    bound = (64 / 8 + 64) * U
+    check("lin/gemm/stride2^22", y.cpu(), ref, scale=dot_scale(oracle.widen(x).reshape(x.shape),
+                                                              oracle.widen(w).reshape(w.shape), _f32(1e-6)),
+          tol=bound, abs_frac=bound)
