@@ -26,6 +26,7 @@ namespace nrs {
 
 namespace {
 constexpr int kThreads = 256;
+constexpr int kSmallThreads = 64;   // block size of calls below kStreamBytes
 constexpr float kExpM64 = 1.60381089054863785e-28f;  // e^-64
 
 __device__ inline float silu_mul_tail(float g, float u) {
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gat
                                                           int64_t gu_stride, int64_t out_stride) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    const int32_t ci = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * kThreads + threadIdx.x;
+    const int32_t ci = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * (int32_t)blockDim.x + threadIdx.x;
     if (ci >= total) return;
     const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
     const int32_t col = ci - r * cpr;
@@ -74,12 +75,16 @@ hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t i
     for (int64_t r0 = 0; r0 < rows && err == hipSuccess; r0 += max_rows) {
         const int64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
         const int32_t total = (int32_t)(nr * cpr);
-        const int64_t blocks = (total + kThreads - 1) / kThreads;
+        const bool nt = 3 * nr * inter * (long long)esz >= kStreamBytes;
+        // small calls are latency-bound: narrow blocks spread them over more
+        // CUs (measured at the 5-token decode step: 64-thread blocks shorten
+        // the kernel by ~0.07 us; more chunks per thread lengthen it)
+        const int bt = nt ? kThreads : kSmallThreads;
+        const int64_t blocks = (total + bt - 1) / bt;
         const fastdiv dv = make_fastdiv((uint32_t)cpr);
         const char *gu = (const char *)gate_up + r0 * gu_stride * esz;
         char *o = (char *)out + r0 * out_stride * esz;
-        const dim3 grid((unsigned)blocks), block(kThreads);
-        const bool nt = 3 * nr * inter * (long long)esz >= kStreamBytes;
+        const dim3 grid((unsigned)blocks), block(bt);
 #define NRS_SWIGLU(IO, NT)                                                                        \
     hipLaunchKernelGGL((swiglu_kernel<IO, NT>), grid, block, 0, stream, (IO *)o, (const IO *)gu, \
                        total, (int32_t)cpr, dv, inter, gu_stride, out_stride)
