@@ -184,6 +184,18 @@ def test_sample_register_held_rows(dt, vocab):
     sample_parity(lg, 0.8, 64, _u(6, 12), f"sample/{dt}/held{vocab}")
 
 
+@pytest.mark.parametrize("dt,vocab,k", [("bf16", 8192, 64), ("f32", 4096, 64), ("bf16", 3080, 33),
+                                        ("f32", 260, 5), ("bf16", 520, 64)])
+def test_sample_partial_chunk_rounds(dt, vocab, k):
+    # rows whose chunks leave the last round of the 1024 threads partly filled
+    # (or fill it exactly), with k up to one wave's width
+    lg = _logits(9, vocab, 3.0, dt, 21)
+    sample_parity(lg, 0.9, k, _u(9, 22), f"sample/rounds/{dt}/V{vocab}/k{k}")
+    # many ties at the k-th value: the lowest indices are kept
+    t = _logits(4, vocab, 1.0, dt, 23, ties=True)
+    sample_parity(t, 1.0, k, _u(4, 24), f"sample/rounds_ties/{dt}/V{vocab}/k{k}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_sample_ties(dt):
     # integer-valued logits: many equal values, the k-th often tied
