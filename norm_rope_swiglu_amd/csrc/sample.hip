@@ -43,8 +43,12 @@ constexpr int kUnroll = 4;  // chunks in flight per thread in the passes over th
 // Radix digit and histogram replicas: rows streamed from memory take 12-bit
 // digits (4096 bins, 4 replicas), so the first pass usually narrows the
 // candidates enough to skip the rest and one read of the row is saved;
-// register-held rows take 8-bit digits (256 bins, 32 replicas), whose smaller
-// histograms cost less to clear and scan than an extra pass over registers.
+// register-held rows take 8-bit digits (256 bins, 32 replicas; 8 when each
+// thread holds one chunk), whose smaller histograms cost less to clear and scan
+// than an extra pass over registers.  Measured on MI355X: at one chunk per
+// thread (rows up to 8192 bf16) 8 replicas cut a 5 x 3072 call from 8.6 to
+// 8.1 us; with more chunks per thread, or flat rows, fewer replicas lose more to
+// atomics on the same bins than they save.
 constexpr int kHistWords = 16384;
 
 // Order-preserving map of an fp32 value to uint32 (larger value, larger key);
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
     constexpr int kDigitBits = CPT > 0 ? 8 : 12;
-    constexpr int kRep = CPT > 0 ? 32 : 4;
+    constexpr int kRep = CPT == 1 ? 8 : (CPT > 0 ? 32 : 4);
     static_assert((kRep << kDigitBits) <= kHistWords, "histogram fits");
     // bin-major: the replicas of a bin sit on kRep consecutive banks
     __shared__ uint32_t hist[kHistWords];
