@@ -300,6 +300,12 @@ __global__ __launch_bounds__(512, 1) void rmsnorm_linear_gemm_kernel(
 
     // one stage: the fragment turn, a barrier, the multiply turn, a barrier
     auto body = [&](auto steady, int st, const auto &As, const auto &Bs, auto &An, auto &Bn) {
+        // stage st + D into the slot stage st - 1 used, which every wave has
+        // finished reading (its reads completed before the last barrier).
+        // Issued before this stage's fragment reads, which read another slot
+        // (measured: 2-7% faster than issuing after them).
+        const bool more = decltype(steady)::value || st + D < nst;
+        if (more) issue(steady, st + D, An, Bn);
         u32x4 af[KS][TM], bf[KS][TN];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -310,10 +316,6 @@ __global__ __launch_bounds__(512, 1) void rmsnorm_linear_gemm_kernel(
             for (int t = 0; t < TN; ++t)
                 bf[ks][t] = *reinterpret_cast<const u32x4 *>(&Bs[gemm_at<CPR>(brow + t * 16, ks * 4 + g)]);
         }
-        // stage st + D into the slot stage st - 1 used, which every wave has
-        // finished reading (its reads completed before the last barrier)
-        const bool more = decltype(steady)::value || st + D < nst;
-        if (more) issue(steady, st + D, An, Bn);
         wait_lgkmcnt0();
         // this wave's share of stage st + 1 must have landed before the
         // barrier after which the other group reads it
