@@ -22,9 +22,9 @@
 //      buffer take an ordered compaction (a block-wide prefix count per 1024
 //      chunks keeps the lowest-index ties);
 //   3. a sort of the gathered entries by (logit descending, index ascending):
-//      lane exchanges within one wave for up to 64; up to 256, each entry's
-//      rank counted by several threads over slices of the entries, then each
-//      entry moved to its rank; beyond, a bitonic network in LDS;
+//      up to 256 entries, each entry's rank counted by several threads over
+//      slices of the entries, then each entry moved to its rank; beyond, a
+//      bitonic network in LDS;
 //   4. exp((l - l_max) / T) per kept entry, an inclusive block scan, and the
 //      first entry whose prefix exceeds u * total.
 // Rows of up to 8 16-byte chunks per thread (65536 bf16 or 32768 fp32
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t ckey[kThreads];   // kept entries: key, index
     __shared__ __attribute__((aligned(16))) int32_t cidx[kThreads];
     __shared__ float csum[kThreads];       // prefix sums of the kept weights
-    __shared__ int32_t rank_of[kThreads];  // ranks of the kept entries (more than 64)
+    __shared__ int32_t rank_of[kThreads];  // ranks of the kept entries (up to kRankMax)
     __shared__ uint32_t n_gt;
     __shared__ int32_t pick;
 
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     // 1. radix select: find the top_k-th largest key, kDigitBits at a time from
     //    the top (streamed bf16 keys: 12 + 4 bits; fp32: 12 + 12 + 8).  The
     //    remaining digits are left to the sort once every key above the
-    //    selected bin plus the bin itself fits one wave (64), or, for a
+    //    selected bin plus the bin itself fits the counting sort (256), or, for a
     //    streamed row, the 1024-entry gather buffer (with 12-bit digits this
     //    usually happens after the first pass, so a streamed row is read twice:
     //    once counted, once gathered).  The
@@ -318,14 +318,16 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         prefix |= sel[0] << shift;
         pmask |= (nb - 1) << shift;
         need -= sel[1];
-        // the candidates left (the same in every thread): stop early when one
-        // wave can sort them, or, for a streamed row, when they fit the buffer
-        // (a read of the row saved outweighs the larger sort); after the last
-        // digit, whenever they fit the buffer
+        // the candidates left (the same in every thread): stop early when the
+        // counting sort takes them (kRankMax; measured on MI355X, this skips
+        // the second pass over a 5 x 3072 row and beats the extra pass), or,
+        // for a streamed row, when they fit the buffer (a read of the row
+        // saved outweighs the larger sort); after the last digit, whenever
+        // they fit the buffer
         const int cand = (top_k - (int)need) + (int)sel[2];
         const bool last = shift == 32 - kKeyBits;
         fits = cand <= kThreads;
-        const bool stop = last || cand <= 64 || (CPT == 0 && fits);
+        const bool stop = last || cand <= kRankMax || (CPT == 0 && fits);
         __syncthreads();                                        // sel is rewritten next pass
         if (stop) break;
     }
@@ -410,33 +412,9 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     }   // ordered compaction
     __syncthreads();
 
-    // 3. sort of the kept entries: logit descending, index ascending.  Up to
-    //    64 entries are sorted by the first wave alone with a bitonic network of
-    //    lane exchanges (no barrier).
-    if (n_kept <= 64) {
-        if (tid < 64) {
-            uint32_t k = tid < n_kept ? ckey[tid] : 0u;          // below every real key
-            int32_t ix = tid < n_kept ? cidx[tid] : 0x7FFFFFFF;
-            for (int size = 2; size <= 64; size <<= 1) {
-                for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                    const uint32_t ko = __shfl_xor(k, stride, 64);
-                    const int32_t io = __shfl_xor(ix, stride, 64);
-                    // the lower lane of each pair keeps the first of the two in
-                    // the pair's direction (descending when (tid & size) == 0)
-                    const bool mine_first = k > ko || (k == ko && ix < io);
-                    const bool lower = (tid & stride) == 0, up = (tid & size) == 0;
-                    if (mine_first != (lower == up)) {
-                        k = ko;
-                        ix = io;
-                    }
-                }
-            }
-            ckey[tid] = k;
-            cidx[tid] = ix;
-        }
-        __syncthreads();
-    } else if (n_kept <= kRankMax) {
-        // 65 to kRankMax entries: every entry's rank is counted by several
+    // 3. sort of the kept entries: logit descending, index ascending.
+    if (n_kept <= kRankMax) {
+        // up to kRankMax entries: every entry's rank is counted by several
         // threads, each over one slice of the entries (thread t takes entry
         // t % n_kept and slice t / n_kept), the slices' counts meet in LDS,
         // and each entry then moves to its rank.  Measured on MI355X at
