@@ -121,6 +121,28 @@ __device__ inline float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Inclusive prefix over the 64 lanes of a wave (lane order), with DPP only:
+// within each 16-lane row, lane i adds lanes i-1, i-2 and i-3, then (lanes
+// 4..15) the running sum 4 back, then (lanes 8..15) 8 back; rows 1 and 3 add
+// the last lane of the row before them (row_bcast:15), rows 2 and 3 add lane
+// 31 (row_bcast:31).  Lanes a step does not write, and sources before the
+// start of a row, contribute 0.  Checked on MI355X against sequential sums.
+template <int CTRL, int ROWS, int BANKS> __device__ inline int dpp_or0(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, BANKS, true);
+}
+template <typename V> __device__ inline V wave_incl_scan(V v) {
+    auto bits = [](V x) { return __builtin_bit_cast(int, x); };
+    auto val = [](int b) { return __builtin_bit_cast(V, b); };
+    V x = v + val(dpp_or0<0x111, 0xF, 0xF>(bits(v)));   // row_shr:1
+    x += val(dpp_or0<0x112, 0xF, 0xF>(bits(v)));         // row_shr:2
+    x += val(dpp_or0<0x113, 0xF, 0xF>(bits(v)));         // row_shr:3
+    x += val(dpp_or0<0x114, 0xF, 0xE>(bits(x)));         // row_shr:4, lanes 4..15
+    x += val(dpp_or0<0x118, 0xF, 0xC>(bits(x)));         // row_shr:8, lanes 8..15
+    x += val(dpp_or0<0x142, 0xA, 0xF>(bits(x)));         // row_bcast:15 into rows 1, 3
+    x += val(dpp_or0<0x143, 0xC, 0xF>(bits(x)));         // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Division of 0 <= n < 2^31 by a fixed 1 <= d < 2^31 with a multiply-high
 // (Granlund and Montgomery, "Division by invariant integers using
 // multiplication", PLDI 1994: the round-up variant with a 33-bit multiplier,
