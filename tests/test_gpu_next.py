@@ -197,6 +197,16 @@ def test_sample_partial_chunk_rounds(dt, vocab, k):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("vocab,k", [(3072, 65), (3072, 128), (32000, 256), (151936, 200)])
+def test_sample_mid_k(dt, vocab, k):
+    # k past one wave: the counting sort (up to 256 gathered entries) with the
+    # block-wide scan, and a streamed row gathering more than one wave
+    rows = 4 if vocab > 50000 else 12
+    lg = _logits(rows, vocab, 3.0, dt, 31)
+    sample_parity(lg, 1.1, k, _u(rows, 32), f"sample/midk/{dt}/V{vocab}/k{k}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_sample_ties(dt):
     # integer-valued logits: many equal values, the k-th often tied
     lg = _logits(40, 3072, 2.0, dt, 3, ties=True)
