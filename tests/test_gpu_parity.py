@@ -170,9 +170,12 @@ def _rand(shape, dt, seed=0, scale=1.0):
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("hidden", [8, 64, 8 * (3 * 64 + 5), 4096 + 8, 8192, 16384, 65536])
+@pytest.mark.parametrize("hidden", [8, 64, 520, 1032, 8 * (3 * 64 + 5), 4096 + 8, 8192, 16384,
+                                    65536])
 def test_norm_widths(dt, hidden):
-    # lane tails, every wave-path width class, and the block-per-row path
+    # lane tails, every wave-path width class (bf16 rows with a residual of
+    # 65-256 chunks: one wave per row, 2 or 4 chunks per thread, part-empty
+    # last chunk), and the block-per-row path
     if dt == torch.float32 and hidden > 32768:
         hidden = 32768
     rows = 37
