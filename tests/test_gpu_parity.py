@@ -284,10 +284,14 @@ def test_mrope_packed_qkv_streams_and_extremes():
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 0), (64, (32, 0, 0), 1, 1),
-                                          (128, (0, 0, 64), 2, 5), (256, (32, 48, 48), 4, 2),
-                                          (512, (64, 96, 96), 2, 1)])
+@pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 0), (32, (4, 6, 6), 2, 3),
+                                          (48, (8, 8, 8), 3, 1), (64, (32, 0, 0), 1, 1),
+                                          (64, (8, 12, 12), 100, 40), (128, (0, 0, 64), 2, 5),
+                                          (256, (32, 48, 48), 4, 2), (512, (64, 96, 96), 2, 1)])
 def test_mrope_shapes(dt, D, sec, nq, nkv):
+    # half-heads of 1, 2 or 4 chunks (bf16 D 16/32/64, fp32 D 16/32) take one thread per
+    # chunk with the partner chunk swizzled in from another lane; 140 heads of 64 give
+    # more chunks per token than a block has threads
     T = 77
     q, k = _rand((T, nq, D), dt, 14), _rand((T, max(nkv, 0), D), dt, 15)
     g = torch.Generator().manual_seed(16)
@@ -298,6 +302,23 @@ def test_mrope_shapes(dt, D, sec, nq, nkv):
     check(f"mrope{D}/q", qd, rq, pairs=True)
     if nkv:
         check(f"mrope{D}/k", kd, rk, pairs=True)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_mrope_narrow_heads_streaming(dt):
+    # a streaming-size call (>= 16 MiB: several tokens per block, nontemporal) with
+    # head_dim 64, 8 q / 4 kv heads, and a part-filled last block, checked on sampled tokens
+    T, nq, nkv, D = 16384 + 4, 8, 4, 64
+    q, k = _rand((T, nq, D), dt, 31), _rand((T, nkv, D), dt, 32)
+    pos = torch.arange(T, dtype=torch.int32).repeat(3, 1).contiguous()
+    qd, kd = cuda(q), cuda(k)
+    nrs.mrope(qd, kd, cuda(pos), (8, 12, 12), 1e6)
+    g = torch.Generator().manual_seed(33)
+    sel = torch.cat([torch.arange(8), torch.arange(T - 8, T), torch.randint(0, T, (200,), generator=g)])
+    rq, rk = oracle.mrope(q[sel].contiguous(), k[sel].contiguous(), pos[:, sel].contiguous(),
+                          (8, 12, 12), 1e6)
+    check("mrope_narrow_stream/q", qd.cpu()[sel], rq, pairs=True)
+    check("mrope_narrow_stream/k", kd.cpu()[sel], rk, pairs=True)
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
