@@ -241,9 +241,11 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_narrow_kernel(
 // rotated in place; k is rotated straight into the k cache (k itself is only
 // read, so the rotated k makes a single trip to memory); v is copied into the
 // v cache.  Items are ordered q, then k, then v per block, two 16-byte chunks
-// (a pair-half each) per item, all loads issued before the angle table is
-// built.  A token whose sequence index or slot is out of range writes no
-// cache entry.
+// (a pair-half each) per item.  All loads are issued before the angle table
+// is built, the data first and the token's sequence index and slot after it,
+// so no load waits on another (with the slot read first, the data loads had
+// to wait for it).  A token whose sequence index or slot is out of range
+// writes no cache entry.
 template <typename IO, bool NT>
 __global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
     IO *q, const IO *k, const IO *v, const int32_t *pos, int64_t pos_stride, int64_t tokens,
@@ -263,30 +265,28 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
     const int kv_items = ntok * n_kv * cph;
     const int items = q_items + 2 * kv_items;
 
-    // item i -> source pointer, destination pointer (nullptr: skip), table
-    // slot, and whether it is rotated (q, k) or copied (v)
-    auto locate = [&](int i, IO *&dst, int &tab, bool &rotate) -> const IO * {
-        const int kind = i < q_items ? 0 : (i < q_items + kv_items ? 1 : 2);
-        const int j = kind == 0 ? i : (kind == 1 ? i - q_items : i - q_items - kv_items);
-        const int hpt = kind == 0 ? n_q : n_kv;
-        const int tl = (int)div((uint32_t)j, kind == 0 ? div_q_ipt : div_kv_ipt);
-        const int rem = j - tl * hpt * cph;
-        const int head = (int)div((uint32_t)rem, div_cph);
-        const int c = rem - head * cph;
-        const int64_t tok = tok0 + tl;
-        tab = tl * half + c * VEC;
-        rotate = kind != 2;
+    // item i -> its source (elements j.. of the pair-halves), kind (0 q, 1 k,
+    // 2 v), token, head and chunk; the fastdiv fields are taken by value
+    // (selecting between structs by address put one on the stack)
+    const uint32_t qm = div_q_ipt.m, qs = div_q_ipt.s, kvm = div_kv_ipt.m, kvs = div_kv_ipt.s;
+    auto locate = [&](int i, int &kind, int64_t &tok, int &head, int &c) -> const IO * {
+        kind = i < q_items ? 0 : (i < q_items + kv_items ? 1 : 2);
+        const uint32_t j = (uint32_t)(kind == 0 ? i : (kind == 1 ? i - q_items : i - q_items - kv_items));
+        const uint32_t m = kind == 0 ? qm : kvm, sh = kind == 0 ? qs : kvs;
+        const int tl = (int)((__umulhi(j, m) + j) >> sh);
+        const int rem = (int)j - tl * (kind == 0 ? n_q : n_kv) * cph;
+        head = (int)div((uint32_t)rem, div_cph);
+        c = rem - head * cph;
+        tok = tok0 + tl;
         const int64_t off = (int64_t)head * head_dim + c * VEC;
-        if (kind == 0) {
-            dst = q + tok * q_stride + off;
-            return dst;
-        }
-        const int64_t b = seq_idx[tok], s = slot[tok];
-        dst = (b >= 0 && b < n_seqs && s >= 0 && s < max_seq)
-                  ? (kind == 1 ? k_cache : v_cache) + ((b * n_kv + head) * max_seq + s) * head_dim +
-                        c * VEC
-                  : nullptr;
-        return (kind == 1 ? k + tok * k_stride : v + tok * v_stride) + off;
+        return (kind == 0 ? q + tok * q_stride : (kind == 1 ? k + tok * k_stride : v + tok * v_stride)) + off;
+    };
+    // destination of an item once its token's sequence index and slot are in
+    // (nullptr: out of range, nothing written)
+    auto dest = [&](const IO *src, int kind, int head, int c, int64_t b, int64_t s) -> IO * {
+        if (kind == 0) return const_cast<IO *>(src);
+        if (b < 0 || b >= n_seqs || s < 0 || s >= max_seq) return nullptr;
+        return (kind == 1 ? k_cache : v_cache) + ((b * n_kv + head) * max_seq + s) * head_dim + c * VEC;
     };
     auto finish = [&](IO *dst, int tab, bool rotate, const u32x4 &lo, const u32x4 &hi) {
         u32x4 olo = lo, ohi = hi;
@@ -295,34 +295,157 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
         store16_policy<NT>(dst + half, ohi);
     };
 
-    // 1. this thread's first item: issue its loads before anything else
-    IO *d0 = nullptr;
-    int tab0 = 0;
-    bool rot0 = false;
+    // 1. this thread's first item: its two loads (a token's k and v exist
+    //    whatever its cache slot), then its token's sequence index and slot,
+    //    with no wait between them
+    const IO *s0 = nullptr;
+    int kind0 = 0, head0 = 0, c0 = 0;
+    int64_t t0 = tok0;
     u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
     if (tid < items) {
-        const IO *src = locate(tid, d0, tab0, rot0);
-        if (d0) {
-            lo0 = load16_policy<NT>(src);
-            hi0 = load16_policy<NT>(src + half);
-        }
+        s0 = locate(tid, kind0, t0, head0, c0);
+        lo0 = load16_policy<NT>(s0);
+        hi0 = load16_policy<NT>(s0 + half);
     }
+    const int64_t b0 = seq_idx[t0], sl0 = slot[t0];   // t0 = tok0 for idle threads: no branch
 
     // 2. the block's angle table
     build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half, fr);
     __syncthreads();
 
     // 3. rotate or copy; blocks with more items than threads loop over the rest
-    if (d0) finish(d0, tab0, rot0, lo0, hi0);
+    if (s0) {
+        IO *d0 = dest(s0, kind0, head0, c0, b0, sl0);
+        if (d0) finish(d0, (int)(t0 - tok0) * half + c0 * VEC, kind0 != 2, lo0, hi0);
+    }
     for (int i = tid + nthreads; i < items; i += nthreads) {
-        IO *dst;
-        int tab;
-        bool rot;
-        const IO *src = locate(i, dst, tab, rot);
-        if (!dst) continue;
+        int kind, head, c;
+        int64_t tok;
+        const IO *src = locate(i, kind, tok, head, c);
         const u32x4 lo = load16_policy<NT>(src);
         const u32x4 hi = load16_policy<NT>(src + half);
-        finish(dst, tab, rot, lo, hi);
+        IO *dst = dest(src, kind, head, c, seq_idx[tok], slot[tok]);
+        if (dst) finish(dst, (int)(tok - tok0) * half + c * VEC, kind != 2, lo, hi);
+    }
+}
+
+// The KV-cache append for half-heads under a cache line: the chunk-per-lane
+// layout of mrope_narrow_kernel (consecutive lanes, consecutive 16-byte
+// chunks; the pair partner by ds_swizzle) over the items of mrope_kv_kernel:
+// q chunks rotated in place, k chunks rotated into the k cache, v chunks
+// copied into the v cache, in that order per block.  A token whose sequence
+// index or slot is out of range writes no cache chunk.
+template <typename IO, bool NT, int CPH>
+__global__ __launch_bounds__(kMaxThreads) void mrope_kv_narrow_kernel(
+    IO *q, const IO *k, const IO *v, const int32_t *pos, int64_t pos_stride, int64_t tokens,
+    int32_t n_kv, int32_t head_dim, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+    int32_t sec_t, int32_t sec_th, int32_t tpb, int32_t q_cpt, int32_t kv_cpt, fastdiv div_half,
+    fastdiv div_q_cpt, fastdiv div_kv_cpt, IO *k_cache, IO *v_cache, const int32_t *seq_idx,
+    const int32_t *slot, int64_t n_seqs, int64_t max_seq, mrope_freqs fr) {
+    constexpr int VEC = io_traits<IO>::VEC;
+    constexpr int CPHEAD = 2 * CPH;                          // chunks per head
+    constexpr int kSwz = (CPH << 10) | 0x1F;                 // bitmask mode: lane xor CPH
+    static_assert(CPH == 1 || CPH == 2 || CPH == 4, "a head's chunk group must tile a wave");
+    using T = io_traits<IO>;
+    extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
+    const int half = head_dim >> 1;
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;   // a multiple of 64
+    const int64_t tok0 = (int64_t)blockIdx.x * tpb;
+    const int ntok = (int)((tokens - tok0) < tpb ? (tokens - tok0) : tpb);
+    const int q_items = ntok * q_cpt;
+    const int kv_items = ntok * kv_cpt;
+    const int items = q_items + 2 * kv_items;
+
+    // item i -> its source chunk, kind (0 q, 1 k, 2 v), token, chunk within
+    // the token's heads, table slot and half; the fastdiv fields are taken by
+    // value (selecting between the two structs by address put one on the stack)
+    const uint32_t qm = div_q_cpt.m, qs = div_q_cpt.s, kvm = div_kv_cpt.m, kvs = div_kv_cpt.s;
+    auto locate = [&](int i, int &kind, int64_t &tok, int &rem, int &tab, bool &upper) -> const IO * {
+        kind = i < q_items ? 0 : (i < q_items + kv_items ? 1 : 2);
+        const uint32_t j = (uint32_t)(kind == 0 ? i : (kind == 1 ? i - q_items : i - q_items - kv_items));
+        const uint32_t m = kind == 0 ? qm : kvm, sh = kind == 0 ? qs : kvs;
+        const int tl = (int)((__umulhi(j, m) + j) >> sh);
+        rem = (int)j - tl * (kind == 0 ? q_cpt : kv_cpt);
+        const int cc = rem & (CPHEAD - 1);                       // chunk within the head
+        tok = tok0 + tl;
+        upper = cc >= CPH;
+        tab = tl * half + (cc & (CPH - 1)) * VEC;
+        return kind == 0 ? q + tok * q_stride + (int64_t)rem * VEC
+                         : (kind == 1 ? k + tok * k_stride : v + tok * v_stride) + (int64_t)rem * VEC;
+    };
+    // every lane of the wave runs this (the swizzle reads other lanes); dst
+    // nullptr stores nothing
+    auto finish = [&](IO *dst, int tab, bool upper, bool rotate, const u32x4 &own) {
+        u32x4 other;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            other[e] = (unsigned)__builtin_amdgcn_ds_swizzle((int)own[e], kSwz);
+        if (!dst) return;
+        u32x4 out = own;
+        if (rotate) {
+            float a[VEC], b[VEC], o[VEC];
+            T::unpack(own, a);
+            T::unpack(other, b);
+            const f32x2 *t = table + tab;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const f32x2 cs = t[e];
+                o[e] = upper ? __builtin_fmaf(a[e], cs.x, b[e] * cs.y)
+                             : __builtin_fmaf(a[e], cs.x, -(b[e] * cs.y));
+            }
+            out = T::pack(o);
+        }
+        store16_policy<NT>(dst, out);
+    };
+
+    // rounds of U chunks per thread: every source chunk is loaded (a token's
+    // k and v exist whatever its cache slot), then the sequence index and slot
+    // of the k and v chunks, so no load waits on another before the table
+    constexpr int U = narrow_per_thread<NT>();
+    for (int base = 0; base < items; base += U * nthreads) {
+        const IO *src[U];
+        int kind[U], rem[U], tab[U];
+        int64_t tok[U], sb[U], ss[U];
+        bool up[U];
+        u32x4 val[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * nthreads + tid;
+            src[u] = nullptr;
+            kind[u] = rem[u] = tab[u] = 0;
+            tok[u] = tok0;
+            up[u] = false;
+            val[u] = u32x4{0, 0, 0, 0};
+            if (i < items) {
+                src[u] = locate(i, kind[u], tok[u], rem[u], tab[u], up[u]);
+                val[u] = load16_policy<NT>(src[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {   // unconditional (tok0 stands in for idle lanes): no branch
+            sb[u] = seq_idx[tok[u]];    // between the loads, so all of them are in flight together
+            ss[u] = slot[tok[u]];
+        }
+        if (base == 0) {   // uniform: every thread takes the barrier
+            build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half,
+                              fr);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            IO *dst = nullptr;
+            if (src[u]) {
+                if (kind[u] == 0) {
+                    dst = const_cast<IO *>(src[u]);
+                } else if (sb[u] >= 0 && sb[u] < n_seqs && ss[u] >= 0 && ss[u] < max_seq) {
+                    const int head = rem[u] / CPHEAD, cc = rem[u] & (CPHEAD - 1);
+                    dst = (kind[u] == 1 ? k_cache : v_cache) +
+                          ((sb[u] * n_kv + head) * max_seq + ss[u]) * head_dim + cc * VEC;
+                }
+            }
+            finish(dst, tab[u], up[u], kind[u] != 2, val[u]);
+        }
     }
 }
 
@@ -338,6 +461,46 @@ hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t 
     const int per_tok = (n_q + 2 * n_kv) * cph;
     const bool nt = tokens * (long long)(2 * n_q + 4 * n_kv) * head_dim * (dtype == 0 ? 4 : 2) >=
                     kStreamBytes;
+    if (cph == 1 || cph == 2 || cph == 4) {
+        // half-heads under a cache line: mrope_kv_narrow_kernel, chunks per
+        // thread and token blocking as for M-RoPE's narrow kernel
+        const int cpt = 2 * per_tok;
+        const int u = nt ? narrow_per_thread<true>() : narrow_per_thread<false>();
+        int tpb = nt ? 512 * u / cpt : 1;
+        if (tpb < 1) tpb = 1;
+        const int per_block = (tpb * cpt + u - 1) / u;
+        int threads = ((per_block + 63) / 64) * 64;
+        if (threads > kMaxThreads) threads = kMaxThreads;
+        const int64_t blocks = (tokens + tpb - 1) / tpb;
+        const size_t lds = (size_t)tpb * half * sizeof(f32x2);
+        const int q_cpt = 2 * n_q * cph, kv_cpt = 2 * n_kv * cph;
+        const fastdiv dh = make_fastdiv((uint32_t)half),
+                      dq = make_fastdiv((uint32_t)(q_cpt > 0 ? q_cpt : 1)),
+                      dkv = make_fastdiv((uint32_t)(kv_cpt > 0 ? kv_cpt : 1));
+        const dim3 grid((unsigned)blocks), block(threads);
+#define NRS_KV_NARROW(IO, NT, C)                                                                 \
+    hipLaunchKernelGGL((mrope_kv_narrow_kernel<IO, NT, C>), grid, block, lds, stream, (IO *)q,   \
+                       (const IO *)k, (const IO *)v, pos, pos_stride, tokens, n_kv, head_dim,    \
+                       q_stride, k_stride, v_stride, sec_t, sec_t + sec_h, tpb, q_cpt, kv_cpt,   \
+                       dh, dq, dkv, (IO *)k_cache, (IO *)v_cache, seq_idx, slot, n_seqs,         \
+                       max_seq, fr)
+#define NRS_KV_NARROW_C(IO, NT)                                                                  \
+    do {                                                                                         \
+        if (cph == 1) NRS_KV_NARROW(IO, NT, 1);                                                  \
+        else if (cph == 2) NRS_KV_NARROW(IO, NT, 2);                                             \
+        else NRS_KV_NARROW(IO, NT, 4);                                                           \
+    } while (0)
+        if (dtype == 0) {
+            if (nt) NRS_KV_NARROW_C(float, true);
+            else NRS_KV_NARROW_C(float, false);
+        } else {
+            if (nt) NRS_KV_NARROW_C(__bf16, true);
+            else NRS_KV_NARROW_C(__bf16, false);
+        }
+#undef NRS_KV_NARROW_C
+#undef NRS_KV_NARROW
+        return hipGetLastError();
+    }
     // as for M-RoPE, small calls take one token per block (measured at the
     // 5-token decode step: 2.77 -> 2.55 us per call)
     int tpb = nt ? 512 / per_tok : 1;
