@@ -117,7 +117,8 @@ def cpu_baseline(w, n_tokens):
 def op_sweep(dev, K=20, R=11):
     """Per-op launch duration and GB/s on every bandwidth-bound recipe: the
     2048-token prefill, the packed ragged batch and the 32768-token sweep at
-    every width and dtype (head_dim 128).  Each op's K launches are captured
+    every width and dtype (head_dim 128, and M-RoPE again at head_dim 64).
+    Each op's K launches are captured
     in one graph (no host launch cost between them) and rotate over enough
     copies of their buffers to cover 1 GiB, so no launch finds its inputs in
     the 256 MB last-level cache; the graph is replayed R times and the
@@ -134,60 +135,71 @@ def op_sweep(dev, K=20, R=11):
         for H in (512, 1024, 1536, 2048, 4096):
             cases.append((f"sweep_{dt}_h{H}", lambda dt=dt, H=H: W.sweep(device=dev, dtype=dt, hidden=H,
                                                                           head_dim=128, tokens=32768)))
+
+    def time_op(op, w):
+        L = w.layer
+        s = 4 if w.dtype == "f32" else 2
+        T, I = w.tokens, w.inter
+        byts = algorithmic_bytes(op, T, w.hidden, I, w.n_q, w.n_kv, w.head_dim, s)
+        nb = max(1, -(-(1 << 30) // byts))
+        empty = lambda t: torch.empty_like(t)
+        if op == "rmsnorm":
+            sets = [(L.residual.clone(), empty(L.x)) for _ in range(nb)]
+            fn = lambda b: nrs.rmsnorm(b[0], L.gamma, w.eps, out=b[1])
+        elif op == "add_rmsnorm":
+            sets = [(L.x.clone(), L.residual.clone(), empty(L.x), empty(L.x)) for _ in range(nb)]
+            fn = lambda b: nrs.add_rmsnorm(b[0], b[1], L.gamma, w.eps, out=b[2], residual_out=b[3])
+        elif op == "mrope":
+            sets = [(L.q.clone(), L.k.clone()) for _ in range(nb)]
+            fn = lambda b: nrs.mrope(b[0], b[1], w.pos, w.sections, w.theta)
+        else:
+            sets = [(L.gate_up.clone(), torch.empty(T, I, dtype=L.x.dtype, device=dev))
+                    for _ in range(nb)]
+            fn = lambda b: nrs.swiglu(b[0], out=b[1])
+        for b in sets[:2]:
+            fn(b)
+        torch.cuda.synchronize()
+        graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream(dev)
+        with torch.cuda.graph(graph, stream=gs):
+            for i in range(K):
+                fn(sets[i % nb])
+        graph.replay()
+        torch.cuda.synchronize()
+        per, cur = [], torch.cuda.current_stream(dev)    # replays run on the current stream
+        for _ in range(R):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            graph.replay()
+            b.record(cur)
+            torch.cuda.synchronize()
+            per.append(1e3 * a.elapsed_time(b) / K)
+        per.sort()
+        us = per[R // 2]
+        del graph, sets
+        torch.cuda.empty_cache()
+        return {"us": round(us, 2), "p10_us": round(per[R // 10], 2),
+                "p90_us": round(per[R - 1 - R // 10], 2), "buffer_sets": nb,
+                "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
+                "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
     out = []
     for name, make in cases:
         w = make()
-        L = w.layer
-        s = 4 if w.dtype == "f32" else 2
-        T, H, I = w.tokens, w.hidden, w.inter
-        rec = {"workload": name, "tokens": T, "hidden": H, "dtype": w.dtype,
+        rec = {"workload": name, "tokens": w.tokens, "hidden": w.hidden, "dtype": w.dtype,
+               "head_dim": w.head_dim,
                "timing": f"graph of {K} launches over buffer copies covering 1 GiB, "
                          f"median/p10/p90 of {R} replays"}
         for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu"):
-            byts = algorithmic_bytes(op, T, H, I, w.n_q, w.n_kv, w.head_dim, s)
-            nb = max(1, -(-(1 << 30) // byts))
-            empty = lambda t: torch.empty_like(t)
-            if op == "rmsnorm":
-                sets = [(L.residual.clone(), empty(L.x)) for _ in range(nb)]
-                fn = lambda b: nrs.rmsnorm(b[0], L.gamma, w.eps, out=b[1])
-            elif op == "add_rmsnorm":
-                sets = [(L.x.clone(), L.residual.clone(), empty(L.x), empty(L.x)) for _ in range(nb)]
-                fn = lambda b: nrs.add_rmsnorm(b[0], b[1], L.gamma, w.eps, out=b[2], residual_out=b[3])
-            elif op == "mrope":
-                sets = [(L.q.clone(), L.k.clone()) for _ in range(nb)]
-                fn = lambda b: nrs.mrope(b[0], b[1], w.pos, w.sections, w.theta)
-            else:
-                sets = [(L.gate_up.clone(), torch.empty(T, I, dtype=L.x.dtype, device=dev))
-                        for _ in range(nb)]
-                fn = lambda b: nrs.swiglu(b[0], out=b[1])
-            for b in sets[:2]:
-                fn(b)
-            torch.cuda.synchronize()
-            graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream(dev)
-            with torch.cuda.graph(graph, stream=gs):
-                for i in range(K):
-                    fn(sets[i % nb])
-            graph.replay()
-            torch.cuda.synchronize()
-            per, cur = [], torch.cuda.current_stream(dev)    # replays run on the current stream
-            for _ in range(R):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(cur)
-                graph.replay()
-                b.record(cur)
-                torch.cuda.synchronize()
-                per.append(1e3 * a.elapsed_time(b) / K)
-            per.sort()
-            us = per[R // 2]
-            rec[op] = {"us": round(us, 2), "p10_us": round(per[R // 10], 2),
-                       "p90_us": round(per[R - 1 - R // 10], 2), "buffer_sets": nb,
-                       "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
-                       "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-            del graph, sets
-            torch.cuda.empty_cache()
+            rec[op] = time_op(op, w)
+        del w
+        if name.startswith("sweep_"):
+            # M-RoPE again at head_dim 64 (sections 8/12/12), the sweep's other head size
+            w = W.sweep(device=dev, dtype=rec["dtype"], hidden=rec["hidden"], head_dim=64,
+                        tokens=rec["tokens"])
+            rec["mrope_head_dim64"] = time_op("mrope", w)
+            del w
         out.append(rec)
         print("bench sweep: " + json.dumps(rec), file=sys.stderr, flush=True)
-        del w, L
         torch.cuda.empty_cache()
     return out
 

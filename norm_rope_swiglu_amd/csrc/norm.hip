@@ -286,21 +286,24 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
     const float inv_h = (float)(1.0 / (double)hidden);
     int wpr, nch;
     norm_shape(nchunks, LN ? 2 : 1, wpr, nch);
-    // bf16 rows with a residual, of 65-256 chunks, take one wave per row and
-    // 2 or 4 chunks per thread: x and the residual then keep twice the bytes
-    // in flight per wave.  Measured on MI355X (graph-timed, inputs rotated
-    // past the 256 MB cache): add_rmsnorm at 2048 x 2048 7.8 -> 7.0 us,
-    // add_layernorm 8.4 -> 7.7 us, about 1% faster at 32768 rows.  fp32 rows
-    // of the same widths measured slower this way (up to 28% for LayerNorm),
-    // and rows of 512 chunks with 8 chunks per thread 8% slower.
-    if (ADD && sizeof(IO) == 2 && nchunks > 64 && nchunks <= 256) {
-        wpr = 1;
-        nch = nchunks <= 128 ? 2 : 4;
-    }
     IO *Y = (IO *)y, *RO = (IO *)res_out;
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma,
              *B = (const IO *)beta;
     const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
+    // Streaming-size (>= 16 MiB) bf16 calls with a residual, rows of 65-256
+    // chunks, take one wave per row and 2 or 4 chunks per thread: x and the
+    // residual then keep twice the bytes in flight per wave.  Measured on
+    // MI355X (graph-timed, inputs rotated past the 256 MB cache): add_rmsnorm
+    // at 2048 x 2048 7.8 -> 7.0 us, add_layernorm 8.4 -> 7.7 us, about 1%
+    // faster at 32768 rows.  fp32 rows of the same widths measured slower this
+    // way (up to 28% for LayerNorm), rows of 512 chunks with 8 chunks per
+    // thread 8% slower, and small calls too: with it, the 5-token decode
+    // step's 28-layer op set took 183 us instead of 169 (its add_rmsnorm rows
+    // on fewer waves and CUs).
+    if (ADD && sizeof(IO) == 2 && nt && nchunks > 64 && nchunks <= 256) {
+        wpr = 1;
+        nch = nchunks <= 128 ? 2 : 4;
+    }
     if (nchunks <= 32) {
         int seg = 1;
         while (seg < nchunks) seg <<= 1;
