@@ -552,6 +552,12 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
         const int u = nt ? narrow_per_thread<true>() : narrow_per_thread<false>();
         int tpb = nt ? 512 * u / cpt : 1;
         if (tpb < 1) tpb = 1;
+        for (int t = tpb; t >= 1; --t) {   // whole waves, as below
+            if ((t * cpt) % (64 * u) == 0) {
+                tpb = t;
+                break;
+            }
+        }
         const int per_block = (tpb * cpt + u - 1) / u;
         int threads = ((per_block + 63) / 64) * 64;
         if (threads > kMaxThreads) threads = kMaxThreads;
@@ -590,6 +596,15 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
     // ~0.16 us.
     int tpb = nt ? 512 / per_tok : 1;
     if (tpb < 1) tpb = 1;
+    // the most tokens up to that whose items fill whole waves (measured at
+    // 32768 tokens: H = 512 and 1024 bf16 2.5% faster with 8 and 4 tokens a
+    // block than with 10 and 5, which leave half a wave idle)
+    for (int t = tpb; t >= 1; --t) {
+        if ((t * per_tok) % 64 == 0) {
+            tpb = t;
+            break;
+        }
+    }
     int threads = ((tpb * per_tok + 63) / 64) * 64;
     if (threads > kMaxThreads) threads = kMaxThreads;
     const int64_t blocks = (tokens + tpb - 1) / tpb;
