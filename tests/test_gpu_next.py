@@ -102,9 +102,12 @@ def test_kv_append_skips_out_of_range(dtype):
     kv_parity(w, seq_idx=seq, slot=slot, n_seqs=3, max_seq=40, tag=f"kv/skip/{dtype}")
 
 
-@pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 1), (128, (16, 24, 24), 16, 8),
+@pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 1), (32, (4, 6, 6), 2, 3),
+                                          (64, (8, 12, 12), 100, 40), (128, (16, 24, 24), 16, 8),
                                           (256, (32, 48, 48), 4, 2)])
 def test_kv_append_head_shapes(D, sec, nq, nkv):
+    # half-heads of 1, 2 or 4 chunks take one lane per chunk with the pair partner swizzled
+    # in; 100 q + 2 x 40 kv heads of 64 give more chunks per token than a block has threads
     for dt in (torch.float32, torch.bfloat16):
         g = torch.Generator().manual_seed(D)
         T = 37
@@ -116,6 +119,18 @@ def test_kv_append_head_shapes(D, sec, nq, nkv):
         perm = torch.randperm(T, generator=g)
         kv_parity(w, seq_idx=(perm % 2).tolist(), slot=(perm // 2).tolist(), n_seqs=2, max_seq=19,
                   tag=f"kv/shape{D}/{dt}")
+
+
+def test_kv_append_narrow_heads_streaming():
+    # head_dim 64 at a streaming size (two chunks per thread, several tokens per block, a
+    # part-filled last block), slots in reverse order, checked on sampled tokens
+    w = W.sweep(dtype="bf16", hidden=1024, head_dim=64, tokens=8192 + 3, device="cuda")
+    T = w.tokens
+    g = torch.Generator().manual_seed(5)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, T - 2, T - 1]),
+                                   torch.randint(0, T, (60,), generator=g)]))
+    kv_parity(w, seq_idx=[0] * T, slot=list(range(T - 1, -1, -1)), n_seqs=1, max_seq=T,
+              tag="kv/narrow_stream", rows=rows)
 
 
 def test_kv_append_full_size_sampled():
