@@ -77,28 +77,50 @@ def traffic_from_counters(bytes_per_launch):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_tokens):
-    """The oracle, untouched, on the first n_tokens of the batch (one host thread)."""
+def cpu_baseline(w, n_tokens, threads=None):
+    """The oracle, untouched, on the first n_tokens of the batch: once on one
+    host thread, and once with the tokens split into equal row shards, one
+    per thread (the oracle's C functions keep no state, and ctypes drops the
+    GIL around them).  The multi-thread run is the reported value."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
 
     L = w.layer
-    sl = slice(0, n_tokens)
-    x, res, gamma = L.x[sl].cpu(), L.residual[sl].cpu(), L.gamma.cpu()
-    q, k, gu, pos = L.q[sl].cpu(), L.k[sl].cpu(), L.gate_up[sl].cpu(), w.pos[:, sl].cpu().contiguous()
     eps = float(np.float32(w.eps))
-    per_op_ms = {}
-    t_all = time.perf_counter()
-    for op, fn in (("rmsnorm", lambda: oracle.rmsnorm(x, gamma, eps)),
-                   ("add_rmsnorm", lambda: oracle.add_rmsnorm(x, res, gamma, eps)),
-                   ("mrope", lambda: oracle.mrope(q, k, pos, w.sections, w.theta)),
-                   ("swiglu", lambda: oracle.swiglu(gu))):
-        t0 = time.perf_counter()
-        fn()
-        per_op_ms[op] = round(1e3 * (time.perf_counter() - t0), 1)
-    dt = time.perf_counter() - t_all
+    gamma = L.gamma.cpu()
+
+    def shard(a, b):
+        sl = slice(a, b)
+        return (L.x[sl].cpu(), L.residual[sl].cpu(), L.q[sl].cpu(), L.k[sl].cpu(),
+                L.gate_up[sl].cpu(), w.pos[:, sl].cpu().contiguous())
+
+    ops = (("rmsnorm", lambda s: oracle.rmsnorm(s[0], gamma, eps)),
+           ("add_rmsnorm", lambda s: oracle.add_rmsnorm(s[0], s[1], gamma, eps)),
+           ("mrope", lambda s: oracle.mrope(s[2], s[3], s[5], w.sections, w.theta)),
+           ("swiglu", lambda s: oracle.swiglu(s[4])))
     byts = sum(algorithmic_bytes(op, n_tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2)
                for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu"))
+
+    def run(n_threads):
+        cuts = [n_tokens * i // n_threads for i in range(n_threads + 1)]
+        shards = [shard(cuts[i], cuts[i + 1]) for i in range(n_threads)]
+        per_op_ms = {}
+        with ThreadPoolExecutor(n_threads) as ex:
+            t_all = time.perf_counter()
+            for op, fn in ops:
+                t0 = time.perf_counter()
+                list(ex.map(fn, shards))
+                per_op_ms[op] = round(1e3 * (time.perf_counter() - t0), 1)
+            dt = time.perf_counter() - t_all
+        return dt, per_op_ms
+
+    if threads is None:
+        # the host share this process may use (16 per GPU on the box), not every core in it
+        threads = max(1, min(16, os.cpu_count() or 1))
+    dt1, ms1 = run(1)
+    dtn, msn = run(threads)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -107,11 +129,14 @@ def cpu_baseline(w, n_tokens):
                 break
     except OSError:
         pass
-    return {"value": round(byts / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "per_op_ms": per_op_ms, "host_cpu": cpu,
-            "host_threads_available": os.cpu_count(),
+    return {"value": round(byts / dtn / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dtn, 3), "per_op_ms": msn,
+            "single_thread": {"value": round(byts / dt1 / 1e9, 3), "seconds": round(dt1, 2),
+                              "per_op_ms": ms1},
+            "host_cpu": cpu, "host_threads_available": os.cpu_count(),
             "sample": f"first {n_tokens} of {w.tokens} tokens of the step's batch, all four ops, "
-                      "fp64 C oracle on one host thread, same algorithmic-byte count"}
+                      f"fp64 C oracle on {threads} host threads (equal row shards), same "
+                      "algorithmic-byte count; single_thread: the same on one thread"}
 
 
 def op_sweep(dev, K=20, R=11):
