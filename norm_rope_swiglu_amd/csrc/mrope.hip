@@ -12,8 +12,9 @@
 // (token, head, chunk) item; every item reads 16 bytes from each half of its
 // head (elements j..j+VEC-1 and j+D/2..), rotates them and writes them back
 // to the same place.  Each item owns its elements, so the in-place update has
-// no read/write hazard.  The item's two loads are issued first; while they
-// are in flight the block builds its angle table:
+// no read/write hazard.  The item's two loads are issued first, then the
+// block builds its angle table (its position loads queue behind the item
+// loads; loading the positions first measured no faster):
 //   for every (token, pair) of the block the angle p * w_j is formed in fp64
 //   (w_j computed on the host in fp64) and converted to turns, the nearest
 //   whole turn is removed in fp64, and only the reduced fraction, |t| <= 1/2,
@@ -21,7 +22,9 @@
 //   turns).  The (cos, sin) table lives in LDS: one evaluation per token and
 //   pair, shared by all n_q + n_kv heads of the token.
 // q and k are addressed with their own token strides, so they may sit inside
-// a packed qkv projection output.
+// a packed qkv projection output.  Heads whose half is narrower than a cache
+// line take mrope_narrow_kernel below, which keeps the token blocking and the
+// table but gives consecutive lanes consecutive chunks.
 #include "device.hpp"
 #include "kernels.hpp"
 
