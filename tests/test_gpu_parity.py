@@ -283,6 +283,28 @@ def test_mrope_packed_qkv_streams_and_extremes():
     assert torch.equal(d[:, (nq + nkv) * D :], v_before)     # v untouched
 
 
+@pytest.mark.parametrize("dt,D", [(torch.bfloat16, 64), (torch.float32, 32), (torch.bfloat16, 16)])
+def test_mrope_narrow_heads_in_packed_qkv(dt, D):
+    # narrow half-heads (chunk per lane, partner swizzled in) inside a packed qkv row, with
+    # the extreme positions; v must stay untouched
+    T, nq, nkv = 45, 6, 2
+    sec = (D // 8, D // 8, D // 2 - D // 4)
+    qkv = _rand((T, (nq + 2 * nkv) * D), dt, 41)
+    g = torch.Generator().manual_seed(42)
+    pos = torch.randint(-5000, 5000, (3, T), generator=g, dtype=torch.int32)
+    pos[:, :3] = torch.tensor([[0, (1 << 24) - 1, -(1 << 24) + 1]] * 3, dtype=torch.int32)
+    d = cuda(qkv)
+    q = d[:, : nq * D].view(T, nq, D)
+    k = d[:, nq * D : (nq + nkv) * D].view(T, nkv, D)
+    v_before = d[:, (nq + nkv) * D :].clone()
+    nrs.mrope(q, k, cuda(pos), sec, 1e6)
+    rq, rk = oracle.mrope(qkv[:, : nq * D].view(T, nq, D), qkv[:, nq * D : (nq + nkv) * D].view(T, nkv, D),
+                          pos, sec, 1e6)
+    check(f"qkv_narrow{D}/mrope.q", q, rq, pairs=True)
+    check(f"qkv_narrow{D}/mrope.k", k, rk, pairs=True)
+    assert torch.equal(d[:, (nq + nkv) * D :], v_before)
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("D,sec,nq,nkv", [(16, (2, 3, 3), 3, 0), (32, (4, 6, 6), 2, 3),
                                           (48, (8, 8, 8), 3, 1), (64, (32, 0, 0), 1, 1),
