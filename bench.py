@@ -139,7 +139,7 @@ def cpu_baseline(w, n_tokens, threads=None):
                       "algorithmic-byte count; single_thread: the same on one thread"}
 
 
-def op_sweep(dev, K=20, R=11):
+def op_sweep(dev, K=20, R=11, only=None):
     """Per-op launch duration and GB/s on every bandwidth-bound recipe: the
     2048-token prefill, the packed ragged batch and the 32768-token sweep at
     every width and dtype (head_dim 128, and M-RoPE again at head_dim 64).
@@ -209,6 +209,8 @@ def op_sweep(dev, K=20, R=11):
 
     out = []
     for name, make in cases:
+        if only and name not in only:
+            continue
         w = make()
         rec = {"workload": name, "tokens": w.tokens, "hidden": w.hidden, "dtype": w.dtype,
                "head_dim": w.head_dim,
@@ -240,6 +242,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--sweep", metavar="FILE",
                     help="also time every op on every bandwidth-bound recipe, written to FILE as JSON")
+    ap.add_argument("--sweep-only", metavar="NAME", action="append",
+                    help="restrict --sweep to the named recipes (e.g. sweep_bf16_h2048); repeatable")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -484,7 +488,7 @@ def main():
         cpu = cpu_baseline(w, args.cpu_tokens)
 
     if args.sweep:
-        recs = op_sweep(dev)
+        recs = op_sweep(dev, only=args.sweep_only)
         with open(args.sweep, "w") as f:
             json.dump(recs, f, indent=1)
 
