@@ -14,7 +14,9 @@
 // exists in memory.
 //
 // With few rows the product is bound by streaming w from HBM once (2 bytes
-// per weight, 2 * rows flops per weight).  A workgroup owns 16 output
+// per weight, 2 * rows flops per weight).  Up to 8 bf16 rows take plain dot
+// products, one weight row per wave at a time in whole lines (the GEMV
+// kernel below).  Otherwise a workgroup owns 16 output
 // columns; its S waves split the input dimension, each streaming 16-byte
 // chunks of its 16 weight rows as the B operand of a 16x16 MFMA tile while
 // x supplies the A operand (one tile per 16 rows, up to MT = 4 tiles sharing
@@ -161,6 +163,118 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
         }
         const float rs = rsqrtf(__builtin_fmaf(sq, inv_n, eps));
         out[(int64_t)m * out_stride + oc] = (IO)(sum * rs);
+    }
+}
+
+// ---------------------------------------------------------------- decode rows (bf16 GEMV)
+//
+// Up to 8 bf16 rows whose x fits 32 KiB: plain dot products instead of
+// matrix-core tiles.  A 16x16 tile's B operand makes every load instruction
+// read 64 bytes from each of 16 weight rows, half of each 128-byte line;
+// here a wave owns kGemvRowsPerWave weight rows and lane l takes their
+// 16-byte chunks l, l + 64, ..., so every load instruction reads 1 KiB of
+// one weight row, whole lines, and the loads of all the wave's rows are in
+// flight together.  The block stages the x rows in LDS once (their sums of
+// squares come from that copy); the products are v_dot2_f32_bf16 on bf16
+// pairs accumulating in fp32, and each lane's partial sums are added across
+// the wave.  Measured on MI355X (graph of 28 calls with distinct weights,
+// 5 x 2048): 12288 outputs 13.8 -> 11.9 us against the tile kernel, 4096
+// outputs 6.6 -> 6.2 us; the weights are read nontemporal (this pattern ran
+// 5-11% faster so, unlike the tiles' 16-row one), and two rows per wave beat
+// one and four.
+constexpr int kGemvRowsPerWave = 2;
+constexpr int kGemvMaxXChunks = 2048;   // rows x chunks of x staged in LDS: 32 KiB
+
+template <int M, int CPL>
+__global__ __launch_bounds__(256) void rmsnorm_gemv_kernel(
+    __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t nchunks, int64_t n_out,
+    int64_t x_stride, int64_t w_stride, int64_t out_stride, fastdiv div_nchunks, float inv_n,
+    float eps) {
+    constexpr int RPW = kGemvRowsPerWave;
+    constexpr int XPT = (M * CPL + 3) / 4;   // x chunks each thread stages (M * nchunks <= 256 * XPT)
+    extern __shared__ u32x4 xs[];            // [M][nchunks]
+    __shared__ float rs[M];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const u32x4 zero = {0, 0, 0, 0};
+    const int nx = M * nchunks;
+
+    // 1. loads, all branch-free (indices clamped, the extra lanes' data
+    //    dropped below): this thread's x chunks first, then the wave's weight
+    //    chunks, so the x stores to LDS wait for x alone
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+        const int e = min((int)threadIdx.x + 256 * k, nx - 1);
+        const int m = (int)div((uint32_t)e, div_nchunks), c = e - m * nchunks;
+        xv[k] = load16(x + (int64_t)m * x_stride + c * 8);
+    }
+    const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
+    u32x4 wv[RPW][CPL];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int64_t n = min(n0 + j, n_out - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            wv[j][i] = load16_stream(w + n * w_stride + (int64_t)min(lane + 64 * i, nchunks - 1) * 8);
+    }
+    // (threads past the end store the last chunk again, the value it holds:
+    // no branch, so no wait beyond x's own loads)
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) xs[min((int)threadIdx.x + 256 * k, nx - 1)] = xv[k];
+    __syncthreads();
+
+    // 2. each row's 1 / rms from the staged copy (wave w takes rows w, w + 4)
+#pragma unroll
+    for (int m = wave; m < M; m += 4) {
+        float sq = 0.0f;
+        for (int c = lane; c < nchunks; c += 64) {
+            const u32x4 v = xs[m * nchunks + c];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (unsigned)v[p]),
+                                                     __builtin_bit_cast(bf16x2, (unsigned)v[p]), sq, false);
+        }
+        sq = wave_sum(sq);
+        if (lane == 0) rs[m] = rsqrtf(__builtin_fmaf(sq, inv_n, eps));
+    }
+
+    // 3. the products: chunk i of every row meets chunk i of every x row
+    float acc[RPW][M];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[j][m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const bool live = c < nchunks;
+        const int cc = live ? c : nchunks - 1;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+            if (!live) wv[j][i] = zero;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const u32x4 xa = xs[m * nchunks + cc];
+#pragma unroll
+            for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    acc[j][m] = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2, (unsigned)xa[p]),
+                        __builtin_bit_cast(bf16x2, (unsigned)wv[j][i][p]), acc[j][m], false);
+        }
+    }
+    __syncthreads();   // rs is written
+
+    // 4. add across the wave; lane m stores row m's output
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int64_t n = n0 + j;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float sum = wave_sum(acc[j][m]);
+            if (lane == m && n < n_out) out[(int64_t)m * out_stride + n] = (__bf16)(sum * rs[m]);
+        }
     }
 }
 
@@ -453,11 +567,47 @@ hipError_t launch_gemm(void *out, const void *x, const void *w, int64_t rows, in
     return hipGetLastError();
 }
 
+// bf16, at most 8 rows whose x fits kGemvMaxXChunks: the GEMV kernel
+hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, int64_t n_in,
+                       int64_t n_out, int64_t xs, int64_t ws, int64_t os, float inv_n, float eps,
+                       hipStream_t stream) {
+    const int32_t nchunks = (int32_t)(n_in / 8);
+    const int cpl = nchunks <= 64 ? 1 : nchunks <= 128 ? 2 : nchunks <= 256 ? 4 : 8;
+    const int64_t per_block = 4 * kGemvRowsPerWave;
+    const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(256);
+    const size_t lds = (size_t)rows * nchunks * sizeof(u32x4);
+    const fastdiv dn = make_fastdiv((uint32_t)nchunks);
+#define NRS_GEMV(M, C)                                                                           \
+    hipLaunchKernelGGL((rmsnorm_gemv_kernel<M, C>), grid, block, lds, stream, (__bf16 *)out,     \
+                       (const __bf16 *)x, (const __bf16 *)w, nchunks, n_out, xs, ws, os, dn,     \
+                       inv_n, eps)
+#define NRS_GEMV_M(C)                                                                            \
+    switch (rows) {                                                                              \
+        case 1: NRS_GEMV(1, C); break;                                                           \
+        case 2: NRS_GEMV(2, C); break;                                                           \
+        case 3: NRS_GEMV(3, C); break;                                                           \
+        case 4: NRS_GEMV(4, C); break;                                                           \
+        case 5: NRS_GEMV(5, C); break;                                                           \
+        case 6: NRS_GEMV(6, C); break;                                                           \
+        case 7: NRS_GEMV(7, C); break;                                                           \
+        default: NRS_GEMV(8, C); break;                                                          \
+    }
+    if (cpl == 1) NRS_GEMV_M(1)
+    else if (cpl == 2) NRS_GEMV_M(2)
+    else if (cpl == 4) NRS_GEMV_M(4)
+    else NRS_GEMV_M(8)
+#undef NRS_GEMV_M
+#undef NRS_GEMV
+    return hipGetLastError();
+}
+
 template <typename IO>
 hipError_t launch_typed(void *out, const void *x, const void *w, int64_t rows, int64_t n_in,
                         int64_t n_out, int64_t xs, int64_t ws, int64_t os, float eps,
                         hipStream_t stream) {
     const float inv_n = (float)(1.0 / (double)n_in);
+    if (sizeof(IO) == 2 && rows <= 8 && rows * (n_in / 8) <= kGemvMaxXChunks)
+        return launch_gemv(out, x, w, rows, n_in, n_out, xs, ws, os, inv_n, eps, stream);
     if (sizeof(IO) == 2 && rows > kMaxTileRows && xs < kMaxGemmStride && ws < kMaxGemmStride)
         return launch_gemm(out, x, w, rows, n_in, n_out, xs, ws, os, inv_n, eps, stream);
     // fp32 rows (and bf16 rows of very long strides) beyond one launch's 64

@@ -91,6 +91,27 @@ def test_output_widths(n_out):
     lin_parity(x, w, 1e-6, f"lin/out{n_out}")
 
 
+@pytest.mark.parametrize("rows,n_in,n_out", [(1, 8, 1), (3, 4096, 40), (4, 2056, 9), (8, 800, 17),
+                                             (8, 2048, 7), (2, 520, 4099)])
+def test_gemv_shapes(rows, n_in, n_out):
+    # bf16 decode rows (<= 8, x within 2048 chunks): one wave per pair of weight rows,
+    # 1, 2, 4 or 8 chunks per lane with part-filled last chunk groups, blocks of 8 weight
+    # rows with part-filled last blocks, and the largest x staged in LDS
+    x, w = lin_inputs(rows, n_in, n_out, "bf16", 11)
+    lin_parity(x, w, 1e-6, f"lin/gemv/{rows}x{n_in}x{n_out}")
+
+
+def test_gemv_strided_operands():
+    xb, wb = lin_inputs(6, 640, 96, "bf16", 12)
+    x, w = xb[:, 64:576], wb[:, 128:640]            # rows of stride 640, 512 wide
+    y = lin_parity(x, w, 1e-6, "lin/gemv/strided")
+    big = torch.zeros(6, 128, dtype=x.dtype, device="cuda")
+    nrs.rmsnorm_linear(x.cuda(), w.cuda(), 1e-6, out=big[:, 16:112])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, 16:112].cpu(), y)
+    assert torch.all(big[:, :16] == 0) and torch.all(big[:, 112:] == 0)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_strided_operands(dt):
     xb, wb = lin_inputs(12, 640, 96, dt, 5)
