@@ -183,15 +183,17 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
 // 5-11% faster so, unlike the tiles' 16-row one), and two rows per wave beat
 // one and four.
 constexpr int kGemvRowsPerWave = 2;
+constexpr int kGemvWaves = 4;        // waves per block
 constexpr int kGemvMaxXChunks = 2048;   // rows x chunks of x staged in LDS: 32 KiB
 
 template <int M, int CPL>
-__global__ __launch_bounds__(256) void rmsnorm_gemv_kernel(
+__global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
     __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t nchunks, int64_t n_out,
     int64_t x_stride, int64_t w_stride, int64_t out_stride, fastdiv div_nchunks, float inv_n,
     float eps) {
     constexpr int RPW = kGemvRowsPerWave;
-    constexpr int XPT = (M * CPL + 3) / 4;   // x chunks each thread stages (M * nchunks <= 256 * XPT)
+    constexpr int NTH = 64 * kGemvWaves;
+    constexpr int XPT = (M * CPL + kGemvWaves - 1) / kGemvWaves;   // x chunks each thread stages (M * nchunks <= NTH * XPT)
     extern __shared__ u32x4 xs[];            // [M][nchunks]
     __shared__ float rs[M];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -204,11 +206,11 @@ __global__ __launch_bounds__(256) void rmsnorm_gemv_kernel(
     u32x4 xv[XPT];
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
-        const int e = min((int)threadIdx.x + 256 * k, nx - 1);
+        const int e = min((int)threadIdx.x + NTH * k, nx - 1);
         const int m = (int)div((uint32_t)e, div_nchunks), c = e - m * nchunks;
         xv[k] = load16(x + (int64_t)m * x_stride + c * 8);
     }
-    const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * RPW;
     u32x4 wv[RPW][CPL];
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
@@ -220,12 +222,12 @@ __global__ __launch_bounds__(256) void rmsnorm_gemv_kernel(
     // (threads past the end store the last chunk again, the value it holds:
     // no branch, so no wait beyond x's own loads)
 #pragma unroll
-    for (int k = 0; k < XPT; ++k) xs[min((int)threadIdx.x + 256 * k, nx - 1)] = xv[k];
+    for (int k = 0; k < XPT; ++k) xs[min((int)threadIdx.x + NTH * k, nx - 1)] = xv[k];
     __syncthreads();
 
-    // 2. each row's 1 / rms from the staged copy (wave w takes rows w, w + 4)
+    // 2. each row's 1 / rms from the staged copy (wave w takes rows w, w + kGemvWaves, ...)
 #pragma unroll
-    for (int m = wave; m < M; m += 4) {
+    for (int m = wave; m < M; m += kGemvWaves) {
         float sq = 0.0f;
         for (int c = lane; c < nchunks; c += 64) {
             const u32x4 v = xs[m * nchunks + c];
@@ -573,8 +575,8 @@ hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, in
                        hipStream_t stream) {
     const int32_t nchunks = (int32_t)(n_in / 8);
     const int cpl = nchunks <= 64 ? 1 : nchunks <= 128 ? 2 : nchunks <= 256 ? 4 : 8;
-    const int64_t per_block = 4 * kGemvRowsPerWave;
-    const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(256);
+    const int64_t per_block = kGemvWaves * kGemvRowsPerWave;
+    const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(64 * kGemvWaves);
     const size_t lds = (size_t)rows * nchunks * sizeof(u32x4);
     const fastdiv dn = make_fastdiv((uint32_t)nchunks);
 #define NRS_GEMV(M, C)                                                                           \
