@@ -184,6 +184,10 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
 // one and four.
 constexpr int kGemvRowsPerWave = 2;
 constexpr int kGemvWaves = 4;        // waves per block
+constexpr int kGemvTurns = 1;        // weight-row pairs each wave takes in turn (the next
+                                     // pair's loads issued before this pair's products;
+                                     // 2 and 3 turns measured no faster: x is staged once
+                                     // per block either way, from L2)
 constexpr int kGemvMaxXChunks = 2048;   // rows x chunks of x staged in LDS: 32 KiB
 
 template <int M, int CPL>
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
     float eps) {
     constexpr int RPW = kGemvRowsPerWave;
     constexpr int NTH = 64 * kGemvWaves;
+    constexpr int IT = kGemvTurns;
     constexpr int XPT = (M * CPL + kGemvWaves - 1) / kGemvWaves;   // x chunks each thread stages (M * nchunks <= NTH * XPT)
     extern __shared__ u32x4 xs[];            // [M][nchunks]
     __shared__ float rs[M];
@@ -210,15 +215,21 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
         const int m = (int)div((uint32_t)e, div_nchunks), c = e - m * nchunks;
         xv[k] = load16(x + (int64_t)m * x_stride + c * 8);
     }
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * RPW;
-    u32x4 wv[RPW][CPL];
+    // weight row j of the wave's turn `it`; turns interleave the block's waves
+    auto row_of = [&](int it, int j) -> int64_t {
+        return (((int64_t)blockIdx.x * IT + it) * kGemvWaves + wave) * RPW + j;
+    };
+    u32x4 wv[IT > 1 ? 2 : 1][RPW][CPL];   // the turn being multiplied and the next one's loads
+    auto load_w = [&](int it, int buf) {
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int64_t n = min(n0 + j, n_out - 1);
+        for (int j = 0; j < RPW; ++j) {
+            const int64_t n = min(row_of(it, j), n_out - 1);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            wv[j][i] = load16_stream(w + n * w_stride + (int64_t)min(lane + 64 * i, nchunks - 1) * 8);
-    }
+            for (int i = 0; i < CPL; ++i)
+                wv[buf][j][i] = load16_stream(w + n * w_stride + (int64_t)min(lane + 64 * i, nchunks - 1) * 8);
+        }
+    };
+    load_w(0, 0);
     // (threads past the end store the last chunk again, the value it holds:
     // no branch, so no wait beyond x's own loads)
 #pragma unroll
@@ -240,42 +251,47 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
         if (lane == 0) rs[m] = rsqrtf(__builtin_fmaf(sq, inv_n, eps));
     }
 
-    // 3. the products: chunk i of every row meets chunk i of every x row
-    float acc[RPW][M];
+    // 3. per turn: the next turn's weight loads, then the products (chunk i of
+    //    every weight row meets chunk i of every x row), then the wave sums;
+    //    lane m stores row m's output
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[j][m] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        const bool live = c < nchunks;
-        const int cc = live ? c : nchunks - 1;
+    for (int it = 0; it < IT; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < IT) load_w(it + 1, buf ^ 1);
+        float acc[RPW][M];
 #pragma unroll
         for (int j = 0; j < RPW; ++j)
-            if (!live) wv[j][i] = zero;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const u32x4 xa = xs[m * nchunks + cc];
+            for (int m = 0; m < M; ++m) acc[j][m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const bool live = c < nchunks;
+            const int cc = live ? c : nchunks - 1;
 #pragma unroll
             for (int j = 0; j < RPW; ++j)
+                if (!live) wv[buf][j][i] = zero;
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    acc[j][m] = __builtin_amdgcn_fdot2_f32_bf16(
-                        __builtin_bit_cast(bf16x2, (unsigned)xa[p]),
-                        __builtin_bit_cast(bf16x2, (unsigned)wv[j][i][p]), acc[j][m], false);
+            for (int m = 0; m < M; ++m) {
+                const u32x4 xa = xs[m * nchunks + cc];
+#pragma unroll
+                for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        acc[j][m] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2, (unsigned)xa[p]),
+                            __builtin_bit_cast(bf16x2, (unsigned)wv[buf][j][i][p]), acc[j][m], false);
+            }
         }
-    }
-    __syncthreads();   // rs is written
-
-    // 4. add across the wave; lane m stores row m's output
+        if (it == 0) __syncthreads();   // rs is written (uniform: every thread takes it)
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int64_t n = n0 + j;
+        for (int j = 0; j < RPW; ++j) {
+            const int64_t n = row_of(it, j);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float sum = wave_sum(acc[j][m]);
-            if (lane == m && n < n_out) out[(int64_t)m * out_stride + n] = (__bf16)(sum * rs[m]);
+            for (int m = 0; m < M; ++m) {
+                const float sum = wave_sum(acc[j][m]);
+                if (lane == m && n < n_out) out[(int64_t)m * out_stride + n] = (__bf16)(sum * rs[m]);
+            }
         }
     }
 }
@@ -575,7 +591,7 @@ hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, in
                        hipStream_t stream) {
     const int32_t nchunks = (int32_t)(n_in / 8);
     const int cpl = nchunks <= 64 ? 1 : nchunks <= 128 ? 2 : nchunks <= 256 ? 4 : 8;
-    const int64_t per_block = kGemvWaves * kGemvRowsPerWave;
+    const int64_t per_block = kGemvWaves * kGemvRowsPerWave * kGemvTurns;
     const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(64 * kGemvWaves);
     const size_t lds = (size_t)rows * nchunks * sizeof(u32x4);
     const fastdiv dn = make_fastdiv((uint32_t)nchunks);
