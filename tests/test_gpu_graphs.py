@@ -70,16 +70,19 @@ def test_graph_layernorm_and_add_layernorm():
     _replays_match(run, [y, y2, ro])
 
 
-def test_graph_rmsnorm_linear_both_paths():
-    x5, x300 = _bf16((5, 2048), 5), _bf16((300, 512), 6)
+def test_graph_rmsnorm_linear_every_path():
+    # 5 rows: the GEMV; 20 rows: the 16-row matrix-core tiles; 300 rows: the tiled GEMM
+    x5, x20, x300 = _bf16((5, 2048), 5), _bf16((20, 2048), 9), _bf16((300, 512), 6)
     w1, w2 = _bf16((4096, 2048), 7, 0.02), _bf16((384, 512), 8, 0.05)
     y1 = torch.empty(5, 4096, dtype=torch.bfloat16, device="cuda")
+    y3 = torch.empty(20, 4096, dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty(300, 384, dtype=torch.bfloat16, device="cuda")
 
     def run():
         nrs.rmsnorm_linear(x5, w1, 1e-6, out=y1)
+        nrs.rmsnorm_linear(x20, w1, 1e-6, out=y3)
         nrs.rmsnorm_linear(x300, w2, 1e-6, out=y2)
-    _replays_match(run, [y1, y2])
+    _replays_match(run, [y1, y3, y2])
 
 
 def test_graph_softmax_topk_sample():
