@@ -189,6 +189,22 @@ def test_norm_widths(dt, hidden):
     check(f"width{hidden}/add.y", y, ry)
 
 
+@pytest.mark.parametrize("rows,hidden", [(2051, 3080), (2048, 4096), (4099, 1544)])
+def test_norm_streaming_shapes(rows, hidden):
+    # streaming-size bf16 calls (>= 16 MiB) in the shapes chosen for them: rows of 257-512
+    # chunks over 2 waves x 4 chunks (RMSNorm, calls up to 64 MiB), rows of 65-256 chunks
+    # over one wave (with the residual add), part-filled chunk groups and blocks
+    dt = torch.bfloat16
+    x, r = _rand((rows, hidden), dt, 21), _rand((rows, hidden), dt, 22)
+    gamma = (1 + 0.1 * _rand((hidden,), torch.float32, 23)).to(dt)
+    y = nrs.rmsnorm(cuda(x), cuda(gamma), 1e-6)
+    check(f"stream{rows}x{hidden}/rmsnorm", y, oracle.rmsnorm(x, gamma, f32(1e-6)))
+    y, ro = nrs.add_rmsnorm(cuda(x), cuda(r), cuda(gamma), 1e-6)
+    ry, rro = oracle.add_rmsnorm(x, r, gamma, f32(1e-6))
+    check_exact(f"stream{rows}x{hidden}/add.residual_out", ro, rro)
+    check(f"stream{rows}x{hidden}/add.y", y, ry)
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("hidden", [16, 40, 128, 136, 256])
 @pytest.mark.parametrize("rows", [1, 37, 1000])
