@@ -290,19 +290,20 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma,
              *B = (const IO *)beta;
     const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
-    // Streaming-size (>= 16 MiB) bf16 calls with a residual or LayerNorm's two
+    // Streaming-size (>= 16 MiB) calls with a residual or LayerNorm's two
     // moments, rows of 65-256 chunks, take one wave per row and 2 or 4 chunks
     // per thread: each wave keeps more bytes in flight and LayerNorm's
     // moments need no cross-wave step.  Measured on MI355X (graph-timed,
-    // inputs rotated past the 256 MB cache): add_rmsnorm at 2048 x 2048
+    // inputs rotated past the 256 MB cache): add_rmsnorm at 2048 x 2048 bf16
     // 7.8 -> 7.0 us, add_layernorm 8.4 -> 7.7 us, layernorm at 32768 x 1536
-    // and x 2048 9% and 6% faster, add_rmsnorm about 1% at 32768 rows; plain
-    // RMSNorm measured no better this way.  fp32 rows of the same widths measured slower this
-    // way (up to 28% for LayerNorm), rows of 512 chunks with 8 chunks per
-    // thread 8% slower, and small calls too: with it, the 5-token decode
-    // step's 28-layer op set took 183 us instead of 169 (its add_rmsnorm rows
-    // on fewer waves and CUs).
-    if ((ADD || LN) && sizeof(IO) == 2 && nt && nchunks > 64 && nchunks <= 256) {
+    // and x 2048 9% and 6% faster; fp32 at 2048 x 1024 12-14% faster with the
+    // residual, 6% for layernorm (once its 4-chunk loads lost their branch,
+    // above); 1-3% at 32768 rows.  Plain RMSNorm measured no better this way,
+    // rows of 512 chunks with 8 chunks per thread 8% slower with a residual,
+    // and small calls slower too: with it, the 5-token decode step's 28-layer
+    // op set took 183 us instead of 169 (its add_rmsnorm rows on fewer waves
+    // and CUs).
+    if ((ADD || LN) && nt && nchunks > 64 && nchunks <= 256) {
         wpr = 1;
         nch = nchunks <= 128 ? 2 : 4;
     }

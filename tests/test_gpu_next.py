@@ -369,18 +369,18 @@ def test_add_layernorm_in_place():
 
 
 @pytest.mark.parametrize("add", [False, True])
-@pytest.mark.parametrize("H", [1544, 3080])
-def test_layernorm_streaming_ragged_width(add, H):
-    # streaming-size bf16 calls whose rows (193 or 385 chunks) take one wave each with 4 or 8
-    # chunks per thread (8: plain LayerNorm only), the last only partly filled, over a row count
-    # that leaves a part-filled block
+@pytest.mark.parametrize("dt,H", [("bf16", 1544), ("bf16", 3080), ("f32", 1000)])
+def test_layernorm_streaming_ragged_width(add, dt, H):
+    # streaming-size calls whose rows (193 or 385 bf16 chunks, 250 fp32 chunks) take one wave
+    # each with 4 or 8 chunks per thread (8: plain LayerNorm only), the last only partly filled,
+    # over a row count that leaves a part-filled block
     T = 8195
-    x, g, b = _ln_inputs(T, H, "bf16", 12)
-    r = _ln_inputs(T, H, "bf16", 13, offset=1.0)[0] if add else None
+    x, g, b = _ln_inputs(T, H, dt, 12)
+    r = _ln_inputs(T, H, dt, 13, offset=1.0)[0] if add else None
     gen = torch.Generator().manual_seed(14)
     rows = torch.unique(torch.cat([torch.tensor([0, 1, 2, 3, T - 3, T - 2, T - 1]),
                                    torch.randint(0, T, (57,), generator=gen)]))
-    ln_parity(x, g, b, 1e-5, f"{'add_' if add else ''}ln/stream{H}", residual=r, rows=rows)
+    ln_parity(x, g, b, 1e-5, f"{'add_' if add else ''}ln/stream/{dt}/{H}", residual=r, rows=rows)
 
 
 @pytest.mark.parametrize("add", [False, True])
