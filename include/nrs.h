@@ -128,9 +128,9 @@ int nrs_add_layernorm(void *y, void *residual_out, const void *x, const void *re
  *   1 <= out_features < 2^31; strides >= the row widths; eps >= 0, finite.
  *   x and w follow the 16-byte rules above; out needs only element alignment
  *   and any out_stride (it is written element by element).
- * Products are accumulated in fp32 on the matrix cores and each row is scaled
- * by 1/rms at the end; the normalised row is never stored.  out must not
- * overlap x or w.
+ * Products are accumulated in fp32 (on the matrix cores, or as bf16 pair dot
+ * products for up to 8 bf16 rows) and each row is scaled by 1/rms at the end;
+ * the normalised row is never stored.  out must not overlap x or w.
  */
 int nrs_rmsnorm_linear(void *out, const void *x, const void *w, int64_t rows, int64_t in_features,
                        int64_t out_features, int64_t x_stride, int64_t w_stride,
