@@ -189,12 +189,14 @@ def test_norm_widths(dt, hidden):
     check(f"width{hidden}/add.y", y, ry)
 
 
-@pytest.mark.parametrize("rows,hidden", [(2051, 3080), (2048, 4096), (4099, 1544)])
-def test_norm_streaming_shapes(rows, hidden):
-    # streaming-size bf16 calls (>= 16 MiB) in the shapes chosen for them: rows of 257-512
-    # chunks over 2 waves x 4 chunks (RMSNorm, calls up to 64 MiB), rows of 65-256 chunks
-    # over one wave (with the residual add), part-filled chunk groups and blocks
-    dt = torch.bfloat16
+@pytest.mark.parametrize("dt,rows,hidden", [(torch.bfloat16, 2051, 3080), (torch.bfloat16, 2048, 4096),
+                                             (torch.bfloat16, 4099, 1544), (torch.float32, 2051, 1540),
+                                             (torch.float32, 2051, 1000)])
+def test_norm_streaming_shapes(dt, rows, hidden):
+    # streaming-size calls (>= 16 MiB) in the shapes chosen for them: bf16 rows of 257-512
+    # chunks over 2 waves x 4 chunks and fp32 ones over one wave x 8 (RMSNorm, calls up to
+    # 32 MiB), rows of 65-256 chunks over one wave (with the residual add), part-filled
+    # chunk groups and blocks
     x, r = _rand((rows, hidden), dt, 21), _rand((rows, hidden), dt, 22)
     gamma = (1 + 0.1 * _rand((hidden,), torch.float32, 23)).to(dt)
     y = nrs.rmsnorm(cuda(x), cuda(gamma), 1e-6)
