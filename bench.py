@@ -314,9 +314,9 @@ def main():
 
     # per-op launch duration: K launches of one op back to back between two
     # events (launch latency overlaps the previous launch, as in the step),
-    # repeated NREP times; mean and spread over the repeats
+    # repeated NREP times; mean, median, p10 / p90 and extremes over the repeats
     per_op = {}
-    NREP = 5
+    NREP = 11
     for op in ops:
         reps = []
         for _ in range(NREP):
@@ -330,9 +330,10 @@ def main():
         reps.sort()
         mean_us = sum(reps) / NREP
         gbs = op_bytes[op] / (mean_us * 1e-6) / 1e9
-        per_op[op] = {"mean_us": round(mean_us, 2), "min_us": round(reps[0], 2),
-                      "max_us": round(reps[-1], 2), "bytes": op_bytes[op], "GB_s": round(gbs, 1),
-                      "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        per_op[op] = {"mean_us": round(mean_us, 2), "median_us": round(reps[NREP // 2], 2),
+                      "p10_us": round(reps[NREP // 10], 2), "p90_us": round(reps[NREP - 1 - NREP // 10], 2),
+                      "min_us": round(reps[0], 2), "max_us": round(reps[-1], 2), "bytes": op_bytes[op],
+                      "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     print(f"bench: step {step_ms:.3f} ms; " + ", ".join(f"{o} {per_op[o]['mean_us']} us"
           for o in ops), file=sys.stderr, flush=True)
 
