@@ -443,6 +443,33 @@ def main():
             "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del ws, graph
+    # the decode-size sampler recorded in a graph (20 calls over distinct logits), so the time
+    # per call has no host launch cost in it
+    lgs = [torch.randn(5, 3072, device=dev).mul_(4.0).to(torch.bfloat16) for _ in range(20)]
+    gs = torch.cuda.Stream(dev)
+    with torch.cuda.stream(gs):
+        for lg in lgs:
+            nrs.softmax_topk_sample(lg, 0.9, 50, u5, token=tok5)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for lg in lgs:
+            nrs.softmax_topk_sample(lg, 0.9, 50, u5, token=tok5)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / (K * len(lgs))
+    byts = 5 * 3072 * 2 + 5 * 8
+    lin["softmax_topk_sample_5x3072_k50_graph20"] = {
+        "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del lgs, graph
     # the prefill shape: 2048 tokens x 2048 -> 4096 (qkv), bound by the matrix cores
     lin_xp = torch.empty(2048, H, device=dev).normal_().to(torch.bfloat16)
     lin_wp = torch.empty(4096, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
