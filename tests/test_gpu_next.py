@@ -133,6 +133,19 @@ def test_kv_append_narrow_heads_streaming():
               tag="kv/narrow_stream", rows=rows)
 
 
+def test_kv_append_small_tokens_streaming():
+    # 4 q + 2 kv heads of 128 (64 items a token) at a streaming size: 4 tokens per ~256-thread
+    # block with a part-filled last block, slots scattered over two sequences
+    w = W.sweep(dtype="bf16", hidden=512, head_dim=128, tokens=8195, device="cuda")
+    T = w.tokens
+    g = torch.Generator().manual_seed(6)
+    perm = torch.randperm(T, generator=g)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, 2, 3, T - 3, T - 2, T - 1]),
+                                   torch.randint(0, T, (57,), generator=g)]))
+    kv_parity(w, seq_idx=(perm % 2).tolist(), slot=(perm // 2).tolist(), n_seqs=2,
+              max_seq=(T + 1) // 2, tag="kv/small_tokens_stream", rows=rows)
+
+
 def test_kv_append_full_size_sampled():
     w = W.sweep(dtype="bf16", hidden=2048, head_dim=128, tokens=32768, device="cuda")
     g = torch.Generator().manual_seed(3)
