@@ -7,10 +7,6 @@
 
 namespace nrs {
 
-// Grid cap for the row kernels, which walk their rows in a grid-stride loop:
-// 8 blocks of 256 threads per CU on a 256-CU part.
-constexpr int64_t kMaxResidentBlocks = 2048;
-
 // Largest supported head_dim / 2 (frequency pairs per head).
 constexpr int kMaxHalf = 256;
 

@@ -182,23 +182,26 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
 // outputs 6.6 -> 6.2 us; the weights are read nontemporal (this pattern ran
 // 5-11% faster so, unlike the tiles' 16-row one), and two rows per wave beat
 // one and four.
+//
+// A lane holds CPL chunks of each of its weight rows per pass; rows wider
+// than 64 * CPL chunks (CPL = 8: more than 4096 inputs) take NP passes, the
+// next pass's weight loads issued before this pass's products.
 constexpr int kGemvRowsPerWave = 2;
-constexpr int kGemvWaves = 4;        // waves per block
-constexpr int kGemvTurns = 1;        // weight-row pairs each wave takes in turn (the next
-                                     // pair's loads issued before this pair's products;
-                                     // 2 and 3 turns measured no faster: x is staged once
-                                     // per block either way, from L2)
+constexpr int kGemvWaves = 4;           // waves per block
 constexpr int kGemvMaxXChunks = 2048;   // rows x chunks of x staged in LDS: 32 KiB
+constexpr int kGemvMaxPasses = 4;       // 64 lanes x 8 chunks x 4 passes = kGemvMaxXChunks
 
-template <int M, int CPL>
+template <int M, int CPL, int NP>
 __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
     __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t nchunks, int64_t n_out,
     int64_t x_stride, int64_t w_stride, int64_t out_stride, fastdiv div_nchunks, float inv_n,
     float eps) {
     constexpr int RPW = kGemvRowsPerWave;
     constexpr int NTH = 64 * kGemvWaves;
-    constexpr int IT = kGemvTurns;
-    constexpr int XPT = (M * CPL + kGemvWaves - 1) / kGemvWaves;   // x chunks each thread stages (M * nchunks <= NTH * XPT)
+    // x chunks each thread stages: M * nchunks <= M * 64 * CPL * NP <= NTH * XPT
+    constexpr int XPT = (M * CPL * NP + kGemvWaves - 1) / kGemvWaves;
+    static_assert(NP == 1 || CPL == 8, "only 8-chunk lanes take several passes");
+    static_assert(NP <= kGemvMaxPasses, "a row fits kGemvMaxXChunks");
     extern __shared__ u32x4 xs[];            // [M][nchunks]
     __shared__ float rs[M];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
 
     // 1. loads, all branch-free (indices clamped, the extra lanes' data
     //    dropped below): this thread's x chunks first, then the wave's weight
-    //    chunks, so the x stores to LDS wait for x alone
+    //    chunks of the first pass, so the x stores to LDS wait for x alone
     u32x4 xv[XPT];
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
@@ -215,18 +218,16 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
         const int m = (int)div((uint32_t)e, div_nchunks), c = e - m * nchunks;
         xv[k] = load16(x + (int64_t)m * x_stride + c * 8);
     }
-    // weight row j of the wave's turn `it`; turns interleave the block's waves
-    auto row_of = [&](int it, int j) -> int64_t {
-        return (((int64_t)blockIdx.x * IT + it) * kGemvWaves + wave) * RPW + j;
-    };
-    u32x4 wv[IT > 1 ? 2 : 1][RPW][CPL];   // the turn being multiplied and the next one's loads
-    auto load_w = [&](int it, int buf) {
+    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * RPW;   // the wave's first weight row
+    u32x4 wv[NP > 1 ? 2 : 1][RPW][CPL];   // this pass's chunks and the next pass's loads
+    auto load_w = [&](int p, int buf) {
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            const int64_t n = min(row_of(it, j), n_out - 1);
+            const int64_t n = min(row0 + j, n_out - 1);
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                wv[buf][j][i] = load16_stream(w + n * w_stride + (int64_t)min(lane + 64 * i, nchunks - 1) * 8);
+                wv[buf][j][i] = load16_stream(
+                    w + n * w_stride + (int64_t)min(lane + 64 * (i + CPL * p), nchunks - 1) * 8);
         }
     };
     load_w(0, 0);
@@ -251,21 +252,21 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
         if (lane == 0) rs[m] = rsqrtf(__builtin_fmaf(sq, inv_n, eps));
     }
 
-    // 3. per turn: the next turn's weight loads, then the products (chunk i of
-    //    every weight row meets chunk i of every x row), then the wave sums;
-    //    lane m stores row m's output
+    // 3. per pass: the next pass's weight loads, then the products (chunk c
+    //    of every weight row meets chunk c of every x row); then the wave
+    //    sums, and lane m stores row m's output
+    float acc[RPW][M];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < IT) load_w(it + 1, buf ^ 1);
-        float acc[RPW][M];
+    for (int j = 0; j < RPW; ++j)
 #pragma unroll
-        for (int j = 0; j < RPW; ++j)
+        for (int m = 0; m < M; ++m) acc[j][m] = 0.0f;
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[j][m] = 0.0f;
+    for (int p = 0; p < NP; ++p) {
+        const int buf = p & 1;
+        if (p + 1 < NP) load_w(p + 1, buf ^ 1);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
+            const int c = lane + 64 * (i + CPL * p);
             const bool live = c < nchunks;
             const int cc = live ? c : nchunks - 1;
 #pragma unroll
@@ -277,21 +278,21 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
+                    for (int q = 0; q < 4; ++q)
                         acc[j][m] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2, (unsigned)xa[p]),
-                            __builtin_bit_cast(bf16x2, (unsigned)wv[buf][j][i][p]), acc[j][m], false);
+                            __builtin_bit_cast(bf16x2, (unsigned)xa[q]),
+                            __builtin_bit_cast(bf16x2, (unsigned)wv[buf][j][i][q]), acc[j][m], false);
             }
         }
-        if (it == 0) __syncthreads();   // rs is written (uniform: every thread takes it)
+    }
+    __syncthreads();   // rs is written (uniform: every thread takes it)
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const int64_t n = row_of(it, j);
+    for (int j = 0; j < RPW; ++j) {
+        const int64_t n = row0 + j;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float sum = wave_sum(acc[j][m]);
-                if (lane == m && n < n_out) out[(int64_t)m * out_stride + n] = (__bf16)(sum * rs[m]);
-            }
+        for (int m = 0; m < M; ++m) {
+            const float sum = wave_sum(acc[j][m]);
+            if (lane == m && n < n_out) out[(int64_t)m * out_stride + n] = (__bf16)(sum * rs[m]);
         }
     }
 }
@@ -585,32 +586,47 @@ hipError_t launch_gemm(void *out, const void *x, const void *w, int64_t rows, in
     return hipGetLastError();
 }
 
-// bf16, at most 8 rows whose x fits kGemvMaxXChunks: the GEMV kernel
+// bf16, at most 8 rows whose x fits kGemvMaxXChunks: the GEMV kernel.  Lanes
+// take 1, 2, 4 or 8 chunks of a weight row per pass; rows of more than 512
+// chunks (only 1-3 rows fit kGemvMaxXChunks then) take 2-4 passes of 8.
 hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, int64_t n_in,
                        int64_t n_out, int64_t xs, int64_t ws, int64_t os, float inv_n, float eps,
                        hipStream_t stream) {
     const int32_t nchunks = (int32_t)(n_in / 8);
     const int cpl = nchunks <= 64 ? 1 : nchunks <= 128 ? 2 : nchunks <= 256 ? 4 : 8;
-    const int64_t per_block = kGemvWaves * kGemvRowsPerWave * kGemvTurns;
+    const int np = (nchunks + 64 * cpl - 1) / (64 * cpl);
+    const int64_t per_block = kGemvWaves * kGemvRowsPerWave;
     const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(64 * kGemvWaves);
     const size_t lds = (size_t)rows * nchunks * sizeof(u32x4);
     const fastdiv dn = make_fastdiv((uint32_t)nchunks);
-#define NRS_GEMV(M, C)                                                                           \
-    hipLaunchKernelGGL((rmsnorm_gemv_kernel<M, C>), grid, block, lds, stream, (__bf16 *)out,     \
+#define NRS_GEMV(M, C, P)                                                                        \
+    hipLaunchKernelGGL((rmsnorm_gemv_kernel<M, C, P>), grid, block, lds, stream, (__bf16 *)out,  \
                        (const __bf16 *)x, (const __bf16 *)w, nchunks, n_out, xs, ws, os, dn,     \
                        inv_n, eps)
 #define NRS_GEMV_M(C)                                                                            \
     switch (rows) {                                                                              \
-        case 1: NRS_GEMV(1, C); break;                                                           \
-        case 2: NRS_GEMV(2, C); break;                                                           \
-        case 3: NRS_GEMV(3, C); break;                                                           \
-        case 4: NRS_GEMV(4, C); break;                                                           \
-        case 5: NRS_GEMV(5, C); break;                                                           \
-        case 6: NRS_GEMV(6, C); break;                                                           \
-        case 7: NRS_GEMV(7, C); break;                                                           \
-        default: NRS_GEMV(8, C); break;                                                          \
+        case 1: NRS_GEMV(1, C, 1); break;                                                        \
+        case 2: NRS_GEMV(2, C, 1); break;                                                        \
+        case 3: NRS_GEMV(3, C, 1); break;                                                        \
+        case 4: NRS_GEMV(4, C, 1); break;                                                        \
+        case 5: NRS_GEMV(5, C, 1); break;                                                        \
+        case 6: NRS_GEMV(6, C, 1); break;                                                        \
+        case 7: NRS_GEMV(7, C, 1); break;                                                        \
+        default: NRS_GEMV(8, C, 1); break;                                                       \
     }
-    if (cpl == 1) NRS_GEMV_M(1)
+    if (np > 1) {
+        // rows * nchunks <= kGemvMaxXChunks: 2 passes (513-1024 chunks) take
+        // 1-3 rows, 3 and 4 passes (more than 1024 chunks) one row
+        if (rows == 1) {
+            if (np == 2) NRS_GEMV(1, 8, 2);
+            else if (np == 3) NRS_GEMV(1, 8, 3);
+            else NRS_GEMV(1, 8, 4);
+        } else if (rows == 2) {
+            NRS_GEMV(2, 8, 2);
+        } else {
+            NRS_GEMV(3, 8, 2);
+        }
+    } else if (cpl == 1) NRS_GEMV_M(1)
     else if (cpl == 2) NRS_GEMV_M(2)
     else if (cpl == 4) NRS_GEMV_M(4)
     else NRS_GEMV_M(8)

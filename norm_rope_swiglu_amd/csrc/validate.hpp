@@ -9,8 +9,9 @@
 
 namespace nrs {
 
-// Widest rows: 512 threads x 16 chunks of 16 bytes (block-per-row kernel).
-constexpr int64_t kMaxHiddenBytes = (int64_t)512 * 16 * 16;
+// Widest norm rows: 16 waves x 8 chunks of 16 bytes per thread (65536 bf16 or
+// 32768 fp32 elements), the widest shape of the row kernel.
+constexpr int64_t kMaxHiddenBytes = (int64_t)16 * 64 * 8 * 16;
 constexpr int kMaxHeadDim = 512;
 // Row and token counts reach the kernels as 32-bit values and grid sizes.
 constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1;

@@ -84,6 +84,73 @@ def _rows2d(t: torch.Tensor, name: str) -> torch.Tensor:
         raise ValueError(f"{name} must be viewable as [rows, width] with unit inner stride") from e
 
 
+def check_positions(pos: torch.Tensor, tokens: int, device=None) -> None:
+    """pos must be int32 [3, >= tokens] with unit inner stride (temporal,
+    height and width rows), on `device` when one is given.  Pure: reads only
+    metadata, so it runs on CPU and meta tensors too."""
+    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
+        raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    if pos.shape[1] < tokens:
+        raise ValueError(f"pos holds {pos.shape[1]} positions per stream, fewer than the "
+                         f"{tokens} tokens")
+    if device is not None and pos.device != device:
+        raise ValueError("pos must be on the device of the other tensors")
+
+
+def check_decode_layers(layers: list[dict], pos: torch.Tensor) -> tuple:
+    """Shapes of a decode-step graph, checked before anything is recorded.
+
+    Every layer must hold the tensors of layer 0's shapes: in_x, in_residual,
+    in_y, in_residual_out [T, hidden]; in_gamma [hidden]; q [T, n_q, D];
+    k [T, n_kv, D]; gate_up [T, 2 * inter]; act_out [T, inter]; and the
+    post_* set either complete (same shapes as in_*) or absent.  All share one
+    float dtype and device and are contiguous; pos is checked as for mrope.
+    The recorded graph binds raw pointers, so a smaller tensor in any layer
+    would be read or written past its end on every replay.  Returns
+    (T, hidden, inter, n_q, n_kv, D).  Pure: reads only tensor metadata."""
+    if not layers:
+        raise ValueError("no layers")
+    L0 = layers[0]
+    for key in ("in_x", "q", "k", "act_out"):
+        if L0.get(key) is None:
+            raise ValueError(f"layer 0 has no {key}")
+    if L0["in_x"].dim() != 2 or L0["q"].dim() != 3 or L0["k"].dim() != 3 or \
+            L0["act_out"].dim() != 2:
+        raise ValueError("in_x and act_out must be [tokens, width]; q and k [tokens, heads, D]")
+    T, hidden = L0["in_x"].shape
+    nq, D = L0["q"].shape[1], L0["q"].shape[2]
+    nkv = L0["k"].shape[1]
+    inter = L0["act_out"].shape[1]
+    dtype, device = L0["in_x"].dtype, L0["in_x"].device
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"libnrs takes float32 or bfloat16 tensors, not {dtype}")
+    want = {"in_y": (T, hidden), "in_residual_out": (T, hidden), "in_x": (T, hidden),
+            "in_residual": (T, hidden), "in_gamma": (hidden,), "q": (T, nq, D),
+            "k": (T, nkv, D), "gate_up": (T, 2 * inter), "act_out": (T, inter)}
+    post = {"post_y": (T, hidden), "post_residual_out": (T, hidden), "post_x": (T, hidden),
+            "post_residual": (T, hidden), "post_gamma": (hidden,)}
+    for i, L in enumerate(layers):
+        unknown = set(L) - set(_LAYER_KEYS)
+        if unknown:
+            raise ValueError(f"layer {i}: unknown keys {sorted(unknown)}")
+        n_post = sum(L.get(k) is not None for k in post)
+        if n_post not in (0, len(post)):
+            raise ValueError(f"layer {i}: the post_* tensors must be given all together or not at all")
+        for key, shp in (want | (post if n_post else {})).items():
+            t = L.get(key)
+            if t is None:
+                raise ValueError(f"layer {i} has no {key}")
+            if t.dtype != dtype or t.device != device:
+                raise TypeError(f"layer {i} {key}: every tensor must share in_x's dtype and device")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"layer {i} {key}: shape {tuple(t.shape)}, expected {shp} "
+                                 "(layer 0's sizes)")
+            if not t.is_contiguous():
+                raise ValueError(f"layer {i} {key} must be contiguous")
+    check_positions(pos, T, device)
+    return T, hidden, inter, nq, nkv, D
+
+
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
             out: torch.Tensor | None = None) -> torch.Tensor:
     x2 = _rows2d(x, "x")
@@ -214,8 +281,7 @@ def mrope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, sections, theta: 
     for t, n in ((q, "q"), (k, "k")):
         if t.shape[1] > 0 and (t.stride(2) != 1 or t.stride(1) != D):
             raise ValueError(f"{n} heads must be packed: strides (token, {D}, 1)")
-    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
-        raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    check_positions(pos, T)
     _one_dtype(q, k)
     d = _dev(q, k, pos)
     st, sh, sw = (int(s) for s in sections)
@@ -244,8 +310,7 @@ def mrope_kv_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torc
     for t, n in ((seq_idx, "seq_idx"), (slot, "slot")):
         if t.dtype != torch.int32 or t.shape != (T,) or not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous int32 [tokens]")
-    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != 3 or pos.stride(1) != 1:
-        raise ValueError("pos must be int32 [3, >=tokens] with unit inner stride")
+    check_positions(pos, T)
     _one_dtype(q, k, v, k_cache, v_cache)
     d = _dev(q, k, v, pos, k_cache, v_cache, seq_idx, slot)
     st, sh, sw = (int(s) for s in sections)
@@ -347,13 +412,9 @@ def decode_graph(layers: list[dict], pos: torch.Tensor, sections, theta: float, 
     """Record the per-layer op set add_rmsnorm -> mrope -> [add_rmsnorm] ->
     swiglu of every layer into one graph.  `layers` holds, per layer, tensors
     under the nrs_decode_layer field names (post_* optional)."""
-    if not layers:
-        raise ValueError("no layers")
+    T, hidden, inter, nq, nkv, D = check_decode_layers(layers, pos)
     L0 = layers[0]
-    T, hidden = L0["in_x"].shape
-    nq, D = L0["q"].shape[1], L0["q"].shape[2]
-    nkv = L0["k"].shape[1]
-    inter = L0["act_out"].shape[-1]
+    _dev(L0["in_x"], pos)
     keep = [pos]
     arr = (DecodeLayer * len(layers))()
     for i, L in enumerate(layers):
@@ -361,10 +422,6 @@ def decode_graph(layers: list[dict], pos: torch.Tensor, sections, theta: float, 
             t = L.get(key)
             if t is None:
                 continue
-            if t.dtype != L0["in_x"].dtype or t.device != L0["in_x"].device:
-                raise TypeError(f"layer {i} {key}: every tensor must share in_x's dtype and device")
-            if not t.is_contiguous():
-                raise ValueError(f"layer {i} {key} must be contiguous")
             keep.append(t)
             setattr(arr[i], key, t.data_ptr())
     st, sh, sw = (int(s) for s in sections)

@@ -72,6 +72,13 @@ def _ptr(a) -> int:
     return a.ctypes.data if isinstance(a, np.ndarray) else a.data_ptr()
 
 
+def _f32(v: float) -> float:
+    """A scalar argument as the library's C ABI receives it: rounded to fp32
+    (eps and the temperature are fp32 arguments there), then widened, so the
+    oracle computes with the very value the kernels use."""
+    return float(np.float32(v))
+
+
 def widen(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a stored fp32/bf16 tensor (any shape)."""
     t = _cpu(t).contiguous()
@@ -95,7 +102,7 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float) -> np.ndarray:
     rows, hidden = x.shape
     g = _cpu(gamma).contiguous()
     y = np.empty((rows, hidden), dtype=np.float64)
-    lib().oracle_rmsnorm(_ptr(y), _ptr(x), _ptr(g), rows, hidden, x.stride(0), float(eps), _code(x))
+    lib().oracle_rmsnorm(_ptr(y), _ptr(x), _ptr(g), rows, hidden, x.stride(0), _f32(eps), _code(x))
     return y
 
 
@@ -108,7 +115,7 @@ def add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, ep
     y = np.empty((rows, hidden), dtype=np.float64)
     res_out = torch.empty_like(x)
     lib().oracle_add_rmsnorm(_ptr(y), _ptr(res_out), _ptr(x), _ptr(residual), _ptr(g), rows,
-                             hidden, float(eps), _code(x))
+                             hidden, _f32(eps), _code(x))
     return y, res_out
 
 
@@ -122,7 +129,7 @@ def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta, eps: float) -> np.ndar
     assert b is None or b.dtype == x.dtype
     y = np.empty((rows, hidden), dtype=np.float64)
     lib().oracle_layernorm(_ptr(y), _ptr(x), _ptr(g), None if b is None else _ptr(b), rows, hidden,
-                           x.stride(0), float(eps), _code(x))
+                           x.stride(0), _f32(eps), _code(x))
     return y
 
 
@@ -136,7 +143,7 @@ def add_layernorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, 
     y = np.empty((rows, hidden), dtype=np.float64)
     res_out = torch.empty_like(x)
     lib().oracle_add_layernorm(_ptr(y), _ptr(res_out), _ptr(x), _ptr(residual), _ptr(g),
-                               None if b is None else _ptr(b), rows, hidden, float(eps), _code(x))
+                               None if b is None else _ptr(b), rows, hidden, _f32(eps), _code(x))
     return y, res_out
 
 
@@ -148,7 +155,7 @@ def rmsnorm_linear(x: torch.Tensor, w: torch.Tensor, eps: float) -> np.ndarray:
     rows, n_in = x.shape
     out = np.empty((rows, w.shape[0]), dtype=np.float64)
     lib().oracle_rmsnorm_linear(_ptr(out), _ptr(x), _ptr(w), rows, n_in, w.shape[0], x.stride(0),
-                                w.stride(0), float(eps), _code(x))
+                                w.stride(0), _f32(eps), _code(x))
     return out
 
 
@@ -213,7 +220,7 @@ def softmax_topk_sample(logits: torch.Tensor, temperature: float, top_k: int, u,
     cdf = np.empty((rows, top_k), dtype=np.float64)
     lib().oracle_softmax_topk_sample(_ptr(tok), None if probs is None else _ptr(probs), _ptr(kept),
                                      _ptr(cdf), _ptr(x), rows, vocab, x.stride(0),
-                                     float(temperature), int(top_k), _ptr(uu), _code(x))
+                                     _f32(temperature), int(top_k), _ptr(uu), _code(x))
     return tok, probs, kept, cdf
 
 

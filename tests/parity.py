@@ -41,8 +41,22 @@ def check(name: str, y: torch.Tensor, r: np.ndarray, pairs: bool = False, scale=
     fp32; abs_frac * scale is the bf16 fallback bound)."""
     y = y.detach().cpu()
     yd = y.double().numpy().reshape(r.shape)
+    # non-finite values pass only where the oracle holds the same one (NaN for
+    # NaN, an infinity of the same sign); anywhere else they fail, whatever
+    # the error metric would make of them (a NaN compares false with any bar)
+    nonfinite = ~np.isfinite(yd) | ~np.isfinite(r)
+    same = (yd == r) | (np.isnan(yd) & np.isnan(r))
+    if (nonfinite & ~same).any():
+        at = tuple(np.argwhere(nonfinite & ~same)[0])
+        raise AssertionError(f"{name}: non-finite mismatch at {at}: got {yd[at]!r}, "
+                             f"oracle {r[at]!r}")
+    if nonfinite.any():     # matching non-finite values: compare the rest
+        yd, r = np.where(nonfinite, 0.0, yd), np.where(nonfinite, 0.0, r)
+        y = torch.from_numpy(np.where(nonfinite, 0.0, yd)).to(y.dtype)
     rec = {"name": name, "dtype": str(y.dtype).replace("torch.", ""), "n": int(r.size),
            "cosine": cosine(yd, r)}
+    if not np.isfinite(rec["cosine"]):
+        raise AssertionError(f"{name}: cosine similarity is not finite")
     if y.dtype == torch.float32:
         if scale is not None:
             err = np.abs(yd - r) / np.maximum(scale, FLT_MIN)
@@ -51,7 +65,7 @@ def check(name: str, y: torch.Tensor, r: np.ndarray, pairs: bool = False, scale=
         worst = float(err.max()) if err.size else 0.0
         rec["max_rel_err"] = worst
         REPORT.append(rec)
-        if worst > tol:
+        if not np.isfinite(worst) or worst > tol:
             at = np.unravel_index(int(err.argmax()), err.shape)
             raise AssertionError(f"{name}: max relative error {worst:.3e} > {tol} at {at}")
         return rec

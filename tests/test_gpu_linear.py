@@ -92,11 +92,16 @@ def test_output_widths(n_out):
 
 
 @pytest.mark.parametrize("rows,n_in,n_out", [(1, 8, 1), (3, 4096, 40), (4, 2056, 9), (8, 800, 17),
-                                             (8, 2048, 7), (2, 520, 4099)])
+                                             (8, 2048, 7), (2, 520, 4099),
+                                             (1, 8192, 33), (2, 6144, 70), (1, 16384, 9),
+                                             (3, 5456, 17), (1, 12296, 5), (2, 4104, 12),
+                                             (1, 4104, 3)])
 def test_gemv_shapes(rows, n_in, n_out):
     # bf16 decode rows (<= 8, x within 2048 chunks): one wave per pair of weight rows,
     # 1, 2, 4 or 8 chunks per lane with part-filled last chunk groups, blocks of 8 weight
-    # rows with part-filled last blocks, and the largest x staged in LDS
+    # rows with part-filled last blocks, and the largest x staged in LDS; rows of more
+    # than 512 chunks (over 4096 inputs) in 2, 3 or 4 passes of 8 chunks per lane, with
+    # part-filled last passes
     x, w = lin_inputs(rows, n_in, n_out, "bf16", 11)
     lin_parity(x, w, 1e-6, f"lin/gemv/{rows}x{n_in}x{n_out}")
 

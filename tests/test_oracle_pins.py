@@ -105,6 +105,7 @@ def test_rmsnorm_constant_row_closed_form():
     c, eps, H = 0.75, 1e-2, 64
     gamma = t32(rng.uniform(0.5, 1.5, H))
     y = oracle.rmsnorm(t32(np.full((1, H), c)), gamma, eps)[0]
+    eps = float(np.float32(eps))     # the fp32 eps the call carries, widened
     want = gamma.double().numpy() * c / math.sqrt(c * c + eps)
     np.testing.assert_allclose(y, want, rtol=1e-15)
 
@@ -617,7 +618,8 @@ def test_topk_sample_ties_and_boundaries():
 def test_topk_sample_matches_torch_softmax_and_topk(T):
     x = torch.from_numpy(rng.standard_normal((4, 3000)).astype(np.float32) * 4)
     tok, probs, kept, cdf = oracle.softmax_topk_sample(x, T, 50, rng.random(4).astype(np.float32))
-    np.testing.assert_allclose(probs, torch.softmax(x.double() / T, dim=1).numpy(), rtol=1e-12)
+    T32 = float(np.float32(T))       # the fp32 temperature the call carries, widened
+    np.testing.assert_allclose(probs, torch.softmax(x.double() / T32, dim=1).numpy(), rtol=1e-12)
     tk = torch.topk(x.double(), 50, dim=1, sorted=True).indices.numpy()
     assert np.array_equal(kept, tk)
     ren = np.take_along_axis(probs, kept, axis=1)
