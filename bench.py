@@ -8,15 +8,23 @@ rmsnorm -> add_rmsnorm -> mrope (in place) -> swiglu, inputs resident in HBM.
 the same run times the decode-step op set (5 tokens x 28 layers of
 add_rmsnorm -> mrope -> swiglu, and the 4-op layer with the post-attention
 norm) replayed from one hipGraph, plus an empty-kernel graph with the same
-node count as the launch floor.  `next_ops` times the ops built beside the
-step (LayerNorm, M-RoPE + KV-cache append, softmax + top-k sampling, and
-RMSNorm + Linear at the decode step's projection shapes and a prefill shape).
+node count as the launch floor.  `configs` times every op on every
+bandwidth-bound workload (the 2048-token prefill, the packed ragged batch,
+and the 32768-token sweep at hidden 512-4096 in bf16 and fp32, M-RoPE also at
+head_dim 64), each launch graph-timed over buffer copies covering 1 GiB so no
+launch finds its inputs in the 256 MB last-level cache, beside the library's
+calibration kernel (nrs_stream_probe) moving the same bytes in the same
+read/write mix: `frac_of_ceiling`.  `ceilings` gives that kernel's rates at 1
+GiB per stream.  `next_ops` times the ops built beside the step (LayerNorm,
+M-RoPE + KV-cache append, softmax + top-k sampling, and RMSNorm + Linear at
+the decode step's projection shapes and two prefill shapes).
 
 Every duration is taken with HIP events recorded on the stream the kernels
 run on.  The oracle (the fp64 C reference) is timed on a bounded sample of the
 same batch on the host for the CPU baseline.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                       [--configs NAME ...] [--no-decode] [--no-next]
 """
 from __future__ import annotations
 
@@ -32,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
 METRIC = "achieved HBM GB/s (% of peak) per fused op; µs per decode-step op set"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_prefill32k_bf16.json")
 KERNEL_SOURCES = ["norm_rope_swiglu_amd/csrc/swiglu.hip", "norm_rope_swiglu_amd/csrc/device.hpp"]
@@ -139,96 +148,329 @@ def cpu_baseline(w, n_tokens, threads=None):
                       "algorithmic-byte count; single_thread: the same on one thread"}
 
 
-def op_sweep(dev, K=20, R=11, only=None):
-    """Per-op launch duration and GB/s on every bandwidth-bound recipe: the
-    2048-token prefill, the packed ragged batch and the 32768-token sweep at
-    every width and dtype (head_dim 128, and M-RoPE again at head_dim 64).
-    Each op's K launches are captured
-    in one graph (no host launch cost between them) and rotate over enough
-    copies of their buffers to cover 1 GiB, so no launch finds its inputs in
-    the 256 MB last-level cache; the graph is replayed R times and the
-    per-launch time is reported as median, p10 and p90 over the replays.
-    Returns a list of records."""
+# Read and write streams of an op, for the calibration kernel of the same mix:
+# (number of read streams, number of write streams, bytes per stream).
+def stream_mix(op, T, H, I, nq, nkv, D, s):
+    if op in ("rmsnorm", "layernorm"):
+        return 1, 1, T * H * s
+    if op in ("add_rmsnorm", "add_layernorm"):
+        return 2, 2, T * H * s
+    if op == "mrope":
+        return 1, 1, T * (nq + nkv) * D * s
+    if op == "swiglu":
+        return 2, 1, T * I * s
+    if op == "mrope_kv_append":
+        return 1, 1, T * (nq + 2 * nkv) * D * s
+    raise ValueError(op)
+
+
+def time_graph(dev, fn, sets, K=20, R=11):
+    """Per-launch duration of fn over rotating buffer sets: K launches
+    (launch i on set i mod len(sets)) captured in one graph, so no host
+    launch cost sits between them; the graph is replayed R times between HIP
+    events on the replay stream.  Returns median, mean, p10 and p90 in us."""
+    import torch
+
+    for b in sets[:2]:
+        fn(b)
+    torch.cuda.synchronize()
+    graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream(dev)
+    with torch.cuda.graph(graph, stream=gs):
+        for i in range(K):
+            fn(sets[i % len(sets)])
+    graph.replay()
+    torch.cuda.synchronize()
+    per, cur = [], torch.cuda.current_stream(dev)    # replays run on the current stream
+    for _ in range(R):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        graph.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        per.append(1e3 * a.elapsed_time(b) / K)
+    del graph
+    per.sort()
+    return {"us": round(per[R // 2], 2), "mean_us": round(sum(per) / R, 2),
+            "p10_us": round(per[R // 10], 2), "p90_us": round(per[R - 1 - R // 10], 2)}
+
+
+def rotation(nbytes):
+    """Buffer copies an op rotates over so that K launches touch >= 1 GiB of
+    distinct memory: no launch finds its inputs in the 256 MB last-level
+    cache (MALL)."""
+    return max(1, -(-ROTATE_BYTES // max(1, nbytes)))
+
+
+def ceiling(dev, n_read, n_write, nbytes, cache, K=20, R=11):
+    """The calibration kernel (nrs_stream_probe) at a given read/write mix and
+    size, rotated and timed exactly like the ops, fastest of its four
+    patterns; memoised in `cache`."""
     import torch
 
     import norm_rope_swiglu_amd as nrs
+
+    key = (n_read, n_write, nbytes)
+    if key not in cache:
+        nb = rotation(nbytes * (n_read + n_write))
+        mk = lambda: torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        sets = []
+        for _ in range(nb):
+            src = [mk().fill_(0x11) for _ in range(n_read)]
+            sets.append((src, [mk() for _ in range(n_write)]))
+        best, per_variant = None, {}
+        for v in range(4):
+            t = time_graph(dev, lambda b, v=v: nrs.stream_probe(n_read, n_write, b[0], b[1], nbytes, v),
+                           sets, K, R)
+            per_variant[v] = t["us"]
+            if best is None or t["us"] < best["us"]:
+                best = dict(t, variant=v)
+        t = best
+        moved = nbytes * (n_read + n_write)
+        t.update(pattern=f"{n_read} read + {n_write} write streams of {nbytes} B",
+                 GB_s=round(moved / (t["us"] * 1e-6) / 1e9, 1), buffer_sets=nb,
+                 us_by_variant=per_variant)
+        cache[key] = t
+        del sets
+        torch.cuda.empty_cache()
+    return cache[key]
+
+
+def op_runner(op, w, dev):
+    """(launch function over one buffer set, buffer sets) for one op of a
+    workload; the sets cover >= 1 GiB together (see rotation)."""
+    import torch
+
+    import norm_rope_swiglu_amd as nrs
+
+    L = w.layer
+    s = 4 if w.dtype == "f32" else 2
+    byts = algorithmic_bytes(op, w.tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, s)
+    nb = rotation(byts)
+    empty = torch.empty_like
+    if op == "rmsnorm":
+        sets = [(L.residual.clone(), empty(L.x)) for _ in range(nb)]
+        return (lambda b: nrs.rmsnorm(b[0], L.gamma, w.eps, out=b[1])), sets, byts
+    if op == "add_rmsnorm":
+        sets = [(L.x.clone(), L.residual.clone(), empty(L.x), empty(L.x)) for _ in range(nb)]
+        return (lambda b: nrs.add_rmsnorm(b[0], b[1], L.gamma, w.eps, out=b[2], residual_out=b[3])), sets, byts
+    if op == "mrope":
+        sets = [(L.q.clone(), L.k.clone()) for _ in range(nb)]
+        return (lambda b: nrs.mrope(b[0], b[1], w.pos, w.sections, w.theta)), sets, byts
+    if op == "swiglu":
+        sets = [(L.gate_up.clone(), torch.empty(w.tokens, w.inter, dtype=L.x.dtype, device=dev))
+                for _ in range(nb)]
+        return (lambda b: nrs.swiglu(b[0], out=b[1])), sets, byts
+    raise ValueError(op)
+
+
+def measure_op(dev, op, w, ceil_cache, K=20, R=11):
+    """One op on one workload: graph-timed with rotation, beside the
+    calibration kernel of the same read/write mix and size."""
+    import torch
+
+    fn, sets, byts = op_runner(op, w, dev)
+    t = time_graph(dev, fn, sets, K, R)
+    del sets
+    torch.cuda.empty_cache()
+    s = 4 if w.dtype == "f32" else 2
+    nr, nw, nbytes = stream_mix(op, w.tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, s)
+    c = ceiling(dev, nr, nw, nbytes, ceil_cache, K, R)
+    gbs = byts / (t["us"] * 1e-6) / 1e9
+    t.update(bytes=byts, GB_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
+             ceiling_us=c["us"], ceiling_GB_s=c["GB_s"],
+             frac_of_ceiling=round(c["us"] / t["us"], 4))
+    return t
+
+
+def config_cases(dev):
+    """The bandwidth-bound workloads: the 2048-token prefill, the packed ragged
+    batch, and the 32768-token sweep at every width and dtype (head_dim 128;
+    M-RoPE again at head_dim 64)."""
     import workloads as W
 
     cases = [("prefill_bf16", lambda: W.prefill(device=dev)),
              ("ragged_bf16", lambda: W.ragged(device=dev))]
     for dt in ("bf16", "f32"):
         for H in (512, 1024, 1536, 2048, 4096):
-            cases.append((f"sweep_{dt}_h{H}", lambda dt=dt, H=H: W.sweep(device=dev, dtype=dt, hidden=H,
-                                                                          head_dim=128, tokens=32768)))
+            cases.append((f"sweep_{dt}_h{H}", lambda dt=dt, H=H: W.sweep(
+                device=dev, dtype=dt, hidden=H, head_dim=128, tokens=32768)))
+    return cases
 
-    def time_op(op, w):
-        L = w.layer
-        s = 4 if w.dtype == "f32" else 2
-        T, I = w.tokens, w.inter
-        byts = algorithmic_bytes(op, T, w.hidden, I, w.n_q, w.n_kv, w.head_dim, s)
-        nb = max(1, -(-(1 << 30) // byts))
-        empty = lambda t: torch.empty_like(t)
-        if op == "rmsnorm":
-            sets = [(L.residual.clone(), empty(L.x)) for _ in range(nb)]
-            fn = lambda b: nrs.rmsnorm(b[0], L.gamma, w.eps, out=b[1])
-        elif op == "add_rmsnorm":
-            sets = [(L.x.clone(), L.residual.clone(), empty(L.x), empty(L.x)) for _ in range(nb)]
-            fn = lambda b: nrs.add_rmsnorm(b[0], b[1], L.gamma, w.eps, out=b[2], residual_out=b[3])
-        elif op == "mrope":
-            sets = [(L.q.clone(), L.k.clone()) for _ in range(nb)]
-            fn = lambda b: nrs.mrope(b[0], b[1], w.pos, w.sections, w.theta)
-        else:
-            sets = [(L.gate_up.clone(), torch.empty(T, I, dtype=L.x.dtype, device=dev))
-                    for _ in range(nb)]
-            fn = lambda b: nrs.swiglu(b[0], out=b[1])
-        for b in sets[:2]:
-            fn(b)
-        torch.cuda.synchronize()
-        graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream(dev)
-        with torch.cuda.graph(graph, stream=gs):
-            for i in range(K):
-                fn(sets[i % nb])
-        graph.replay()
-        torch.cuda.synchronize()
-        per, cur = [], torch.cuda.current_stream(dev)    # replays run on the current stream
-        for _ in range(R):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(cur)
-            graph.replay()
-            b.record(cur)
-            torch.cuda.synchronize()
-            per.append(1e3 * a.elapsed_time(b) / K)
-        per.sort()
-        us = per[R // 2]
-        del graph, sets
-        torch.cuda.empty_cache()
-        return {"us": round(us, 2), "p10_us": round(per[R // 10], 2),
-                "p90_us": round(per[R - 1 - R // 10], 2), "buffer_sets": nb,
-                "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
-                "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+def measure_configs(dev, ceil_cache, only=None, reuse=None, K=20, R=11):
+    """Every op on every bandwidth-bound workload (config_cases).  `reuse`
+    maps a case name to an already generated workload."""
+    import torch
+
+    import workloads as W
 
     out = []
-    for name, make in cases:
+    for name, make in config_cases(dev):
         if only and name not in only:
             continue
-        w = make()
-        rec = {"workload": name, "tokens": w.tokens, "hidden": w.hidden, "dtype": w.dtype,
-               "head_dim": w.head_dim,
-               "timing": f"graph of {K} launches over buffer copies covering 1 GiB, "
-                         f"median/p10/p90 of {R} replays"}
+        w = (reuse or {}).get(name) or make()
+        rec = {"workload": name, "tokens": w.tokens, "hidden": w.hidden, "inter": w.inter,
+               "dtype": w.dtype, "head_dim": w.head_dim, "n_q": w.n_q, "n_kv": w.n_kv,
+               "timing": f"graph of {K} launches over buffer copies covering >= 1 GiB, "
+                         f"median/p10/p90 of {R} replays; ceiling: nrs_stream_probe at the "
+                         "op's read/write mix and size, timed the same way"}
         for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu"):
-            rec[op] = time_op(op, w)
+            rec[op] = measure_op(dev, op, w, ceil_cache, K, R)
         del w
+        torch.cuda.empty_cache()
         if name.startswith("sweep_"):
             # M-RoPE again at head_dim 64 (sections 8/12/12), the sweep's other head size
             w = W.sweep(device=dev, dtype=rec["dtype"], hidden=rec["hidden"], head_dim=64,
                         tokens=rec["tokens"])
-            rec["mrope_head_dim64"] = time_op("mrope", w)
+            rec["mrope_head_dim64"] = measure_op(dev, "mrope", w, ceil_cache, K, R)
             del w
+            torch.cuda.empty_cache()
         out.append(rec)
-        print("bench sweep: " + json.dumps(rec), file=sys.stderr, flush=True)
-        torch.cuda.empty_cache()
+        print("bench config: " + json.dumps(rec), file=sys.stderr, flush=True)
     return out
+
+
+def bar_summary(configs, bar=0.8):
+    """Which (workload, op) pairs sit below `bar` of the HBM peak, and the
+    lowest fraction of the matched calibration kernel."""
+    below, worst = [], None
+    for rec in configs:
+        for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu", "mrope_head_dim64"):
+            r = rec.get(op)
+            if r is None:
+                continue
+            if r["frac_of_peak"] < bar:
+                below.append({"workload": rec["workload"], "op": op, "frac_of_peak": r["frac_of_peak"],
+                              "frac_of_ceiling": r["frac_of_ceiling"],
+                              "ceiling_frac_of_peak": round(r["ceiling_GB_s"] / PEAK_HBM_GBS, 4)})
+            if worst is None or r["frac_of_ceiling"] < worst["frac_of_ceiling"]:
+                worst = {"workload": rec["workload"], "op": op, "frac_of_ceiling": r["frac_of_ceiling"]}
+    n = sum(1 for rec in configs for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu",
+                                             "mrope_head_dim64") if op in rec)
+    return {"bar": bar, "pairs": n, "pairs_below_bar": len(below), "below": below,
+            "lowest_frac_of_ceiling": worst}
+
+
+def measure_next(dev, w, ceil_cache, K=20, R=11):
+    """The ops built beside the four-op step, on the step's batch shapes:
+    LayerNorm (plain and fused), M-RoPE + KV-cache append and the sampler over
+    a text-sized vocabulary (graph-timed with rotation, beside the matched
+    calibration kernel); the decode-size sampler and RMSNorm + Linear at the
+    decode step's projection shapes (graphs of distinct inputs); the prefill
+    RMSNorm + Linear, priced against the bf16 matrix-core peak."""
+    import torch
+
+    import norm_rope_swiglu_amd as nrs
+
+    L = w.layer
+    T, H, I, nq, nkv, D, s = w.tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2
+    res = {}
+
+    def rotated(name, fn, sets, byts, mix):
+        t = time_graph(dev, fn, sets, K, R)
+        gbs = byts / (t["us"] * 1e-6) / 1e9
+        t.update(bytes=byts, GB_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if mix is not None:
+            c = ceiling(dev, *mix, ceil_cache, K, R)
+            t.update(ceiling_us=c["us"], ceiling_GB_s=c["GB_s"],
+                     frac_of_ceiling=round(c["us"] / t["us"], 4))
+        res[name] = t
+        torch.cuda.empty_cache()
+
+    beta = torch.empty_like(L.gamma).normal_().mul_(0.1)
+    byts = algorithmic_bytes("layernorm", T, H, I, nq, nkv, D, s)
+    sets = [(L.residual.clone(), torch.empty_like(L.x)) for _ in range(rotation(byts))]
+    rotated("layernorm", lambda b: nrs.layernorm(b[0], L.gamma, beta, 1e-5, out=b[1]), sets, byts,
+            stream_mix("layernorm", T, H, I, nq, nkv, D, s))
+    byts = algorithmic_bytes("add_layernorm", T, H, I, nq, nkv, D, s)
+    sets = [(L.x.clone(), L.residual.clone(), torch.empty_like(L.x), torch.empty_like(L.x))
+            for _ in range(rotation(byts))]
+    rotated("add_layernorm", lambda b: nrs.add_layernorm(b[0], b[1], L.gamma, beta, 1e-5, out=b[2],
+                                                         residual_out=b[3]),
+            sets, byts, stream_mix("add_layernorm", T, H, I, nq, nkv, D, s))
+    del sets
+    # M-RoPE + KV-cache append: one 32768-slot sequence, slot = token index
+    byts = algorithmic_bytes("mrope_kv_append", T, H, I, nq, nkv, D, s)
+    seq0 = torch.zeros(T, dtype=torch.int32, device=dev)
+    slots = torch.arange(T, dtype=torch.int32, device=dev)
+    sets = []
+    for _ in range(rotation(byts)):
+        kc = torch.empty(1, nkv, T, D, dtype=L.k.dtype, device=dev)
+        sets.append((L.q.clone(), L.k.clone(), torch.empty_like(L.k).normal_(), kc, torch.empty_like(kc)))
+    rotated("mrope_kv_append", lambda b: nrs.mrope_kv_append(b[0], b[1], b[2], w.pos, w.sections,
+                                                             w.theta, b[3], b[4], seq0, slots),
+            sets, byts, stream_mix("mrope_kv_append", T, H, I, nq, nkv, D, s))
+    del sets
+    # sampling over a text-sized vocabulary: 256 rows x 151936 bf16 logits (algorithmic
+    # bytes: the logits read once, u read and the token written); ceiling: read-only
+    byts = 256 * 151936 * 2 + 256 * 8
+    sets = [(torch.randn(256, 151936, device=dev).mul_(3.0).to(torch.bfloat16),
+             torch.rand(256, device=dev), torch.empty(256, dtype=torch.int32, device=dev))
+            for _ in range(rotation(byts))]
+    rotated("softmax_topk_sample_256x151936_k50",
+            lambda b: nrs.softmax_topk_sample(b[0], 1.0, 50, b[1], token=b[2]), sets, byts,
+            (1, 0, 256 * 151936 * 2))
+    del sets
+
+    # decode-size calls recorded in graphs over distinct inputs (so no host launch cost and
+    # every call streams its own weights / logits)
+    def graph_calls(name, calls, byts, n):
+        gs = torch.cuda.Stream(dev)
+        with torch.cuda.stream(gs):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for c in calls:
+                c()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        for _ in range(K):
+            graph.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / (K * n)
+        res[name] = {"mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del graph
+
+    lin_x = torch.empty(5, H, device=dev).normal_().to(torch.bfloat16)
+    for n_out in (4096, 12288):
+        ws = [torch.empty(n_out, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
+              for _ in range(28)]
+        yo = torch.empty(5, n_out, dtype=torch.bfloat16, device=dev)
+        graph_calls(f"rmsnorm_linear_5x2048x{n_out}_graph28",
+                    [lambda wt=wt: nrs.rmsnorm_linear(lin_x, wt, 1e-6, out=yo) for wt in ws],
+                    n_out * H * 2 + 5 * H * 2 + 5 * n_out * 2, 28)
+        del ws
+    u5 = torch.rand(5, device=dev)
+    tok5 = torch.empty(5, dtype=torch.int32, device=dev)
+    lgs = [torch.randn(5, 3072, device=dev).mul_(4.0).to(torch.bfloat16) for _ in range(20)]
+    graph_calls("softmax_topk_sample_5x3072_k50_graph20",
+                [lambda lg=lg: nrs.softmax_topk_sample(lg, 0.9, 50, u5, token=tok5) for lg in lgs],
+                5 * 3072 * 2 + 5 * 8, 20)
+    del lgs
+
+    # the prefill projections, bound by the matrix cores
+    for M, N in ((2048, 4096), (32768, 4096)):
+        xp = torch.empty(M, H, device=dev).normal_().to(torch.bfloat16)
+        wp = torch.empty(N, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
+        yp = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t = time_graph(dev, lambda b: nrs.rmsnorm_linear(b[0], b[1], 1e-6, out=b[2]), [(xp, wp, yp)],
+                       K, R)
+        tf = 2 * M * H * N / (t["mean_us"] * 1e-6) / 1e12
+        t.update(TFLOP_s=round(tf, 1), frac_of_peak=round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                 peak="bf16 dense MFMA 2500 TFLOP/s")
+        res[f"rmsnorm_linear_{M}x{H}x{N}"] = t
+        del xp, wp, yp
+    torch.cuda.empty_cache()
+    print(f"bench: next {json.dumps(res)}", file=sys.stderr, flush=True)
+    return res
 
 
 def main():
@@ -240,10 +482,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--sweep", metavar="FILE",
-                    help="also time every op on every bandwidth-bound recipe, written to FILE as JSON")
-    ap.add_argument("--sweep-only", metavar="NAME", action="append",
-                    help="restrict --sweep to the named recipes (e.g. sweep_bf16_h2048); repeatable")
+    ap.add_argument("--no-next", action="store_true", help="skip the ops beyond the four-op step")
+    ap.add_argument("--configs", metavar="NAME", action="append",
+                    help="time only the named bandwidth-bound workloads (e.g. sweep_bf16_h2048, "
+                         "prefill_bf16); repeatable; 'none' skips them")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -311,31 +553,33 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / K
+    print(f"bench: step {step_ms:.3f} ms", file=sys.stderr, flush=True)
+    del y, y2, ro, act, q, k, xn
+    torch.cuda.empty_cache()
 
-    # per-op launch duration: K launches of one op back to back between two
-    # events (launch latency overlaps the previous launch, as in the step),
-    # repeated NREP times; mean, median, p10 / p90 and extremes over the repeats
-    per_op = {}
-    NREP = 11
-    for op in ops:
-        reps = []
-        for _ in range(NREP):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(K):
-                run(op)
-            b.record(stream)
-            torch.cuda.synchronize()
-            reps.append(1e3 * a.elapsed_time(b) / K)
-        reps.sort()
-        mean_us = sum(reps) / NREP
-        gbs = op_bytes[op] / (mean_us * 1e-6) / 1e9
-        per_op[op] = {"mean_us": round(mean_us, 2), "median_us": round(reps[NREP // 2], 2),
-                      "p10_us": round(reps[NREP // 10], 2), "p90_us": round(reps[NREP - 1 - NREP // 10], 2),
-                      "min_us": round(reps[0], 2), "max_us": round(reps[-1], 2), "bytes": op_bytes[op],
-                      "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    print(f"bench: step {step_ms:.3f} ms; " + ", ".join(f"{o} {per_op[o]['mean_us']} us"
-          for o in ops), file=sys.stderr, flush=True)
+    # --- calibration: the streaming kernel at 1 GiB per stream, each mix
+    ceil_cache = {}
+    ceilings = {}
+    for name, (nr, nw) in (("read", (1, 0)), ("write", (0, 1)), ("copy", (1, 1)),
+                           ("read2_write1", (2, 1)), ("read2_write2", (2, 2))):
+        c = ceiling(dev, nr, nw, 1 << 30, ceil_cache)
+        ceilings[name] = {"GB_s": c["GB_s"], "frac_of_peak": round(c["GB_s"] / PEAK_HBM_GBS, 4),
+                          "us": c["us"], "bytes_per_stream": 1 << 30}
+    print(f"bench: ceilings {json.dumps(ceilings)}", file=sys.stderr, flush=True)
+
+    # --- every op on every bandwidth-bound workload (the headline shape is
+    # sweep_bf16_h2048, whose per-op figures are the per_op block)
+    only = args.configs
+    if only is None or only != ["none"]:
+        configs = measure_configs(dev, ceil_cache, only=only, reuse={"sweep_bf16_h2048": w})
+    else:
+        configs = []
+    head = next((r for r in configs if r["workload"] == "sweep_bf16_h2048"), None)
+    if head is None:     # not among the selected workloads: time the headline ops alone
+        head = {op: measure_op(dev, op, w, ceil_cache) for op in ops}
+    per_op = {op: head[op] for op in ops}
+    print("bench: per-op " + ", ".join(f"{o} {per_op[o]['us']} us" for o in ops),
+          file=sys.stderr, flush=True)
 
     # --- decode-step op set, hipGraph replay
     decode = None
@@ -381,144 +625,23 @@ def main():
             floor.close()
         print(f"bench: decode {json.dumps(decode)}", file=sys.stderr, flush=True)
 
-    # --- ops beyond the four-op step, on the same batch
-    next_ops = {}
-    v = torch.empty_like(L.k).normal_()
-    kc = torch.empty(1, nkv, T, D, dtype=L.k.dtype, device=dev)
-    vc = torch.empty_like(kc)
-    seq0 = torch.zeros(T, dtype=torch.int32, device=dev)
-    slots = torch.arange(T, dtype=torch.int32, device=dev)
-    # sampling: the decode step's 5 candidates over a 3072-entry codec vocabulary, and a
-    # text-sized vocabulary at 256 rows (algorithmic bytes: logits read once, u, token)
-    lg_dec = torch.randn(5, 3072, device=dev).mul_(4.0).to(torch.bfloat16)
-    lg_big = torch.randn(256, 151936, device=dev).mul_(3.0).to(torch.bfloat16)
-    u5, u256 = torch.rand(5, device=dev), torch.rand(256, device=dev)
-    tok5 = torch.empty(5, dtype=torch.int32, device=dev)
-    tok256 = torch.empty(256, dtype=torch.int32, device=dev)
-    beta = torch.empty_like(L.gamma).normal_().mul_(0.1)
-    nxt = {"layernorm": (lambda: nrs.layernorm(xn, L.gamma, beta, 1e-5, out=y),
-                         algorithmic_bytes("layernorm", T, H, I, nq, nkv, D, s)),
-           "add_layernorm": (lambda: nrs.add_layernorm(L.x, L.residual, L.gamma, beta, 1e-5, out=y2,
-                                                       residual_out=ro),
-                             algorithmic_bytes("add_layernorm", T, H, I, nq, nkv, D, s)),
-           "mrope_kv_append": (lambda: nrs.mrope_kv_append(q, L.k, v, w.pos, w.sections, w.theta,
-                                                           kc, vc, seq0, slots),
-                               algorithmic_bytes("mrope_kv_append", T, H, I, nq, nkv, D, s)),
-           "softmax_topk_sample_5x3072_k50": (
-               lambda: nrs.softmax_topk_sample(lg_dec, 0.9, 50, u5, token=tok5), 5 * 3072 * 2 + 5 * 8),
-           "softmax_topk_sample_256x151936_k50": (
-               lambda: nrs.softmax_topk_sample(lg_big, 1.0, 50, u256, token=tok256),
-               256 * 151936 * 2 + 256 * 8)}
-    # fused RMSNorm + Linear at the decode step's projection shapes: 5 rows of 2048 into
-    # qkv (4096) and gate_up (12288), one distinct weight per layer for 28 layers (so each
-    # call streams its weight from HBM, 0.5-1.4 GB in all); recorded in a graph, so the
-    # time per call has no host launch cost in it
-    lin_x = torch.empty(5, H, device=dev).normal_().to(torch.bfloat16)
-    lin = {}
-    for n_out in (4096, 12288):
-        ws = [torch.empty(n_out, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
-              for _ in range(28)]
-        yo = torch.empty(5, n_out, dtype=torch.bfloat16, device=dev)
-        gs = torch.cuda.Stream(dev)
-        with torch.cuda.stream(gs):
-            for wt in ws:
-                nrs.rmsnorm_linear(lin_x, wt, 1e-6, out=yo)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=gs):
-            for wt in ws:
-                nrs.rmsnorm_linear(lin_x, wt, 1e-6, out=yo)
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(K):
-            graph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * a.elapsed_time(b) / (K * 28)
-        byts = n_out * H * 2 + 5 * H * 2 + 5 * n_out * 2
-        lin[f"rmsnorm_linear_5x2048x{n_out}_graph28"] = {
-            "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
-            "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        del ws, graph
-    # the decode-size sampler recorded in a graph (20 calls over distinct logits), so the time
-    # per call has no host launch cost in it
-    lgs = [torch.randn(5, 3072, device=dev).mul_(4.0).to(torch.bfloat16) for _ in range(20)]
-    gs = torch.cuda.Stream(dev)
-    with torch.cuda.stream(gs):
-        for lg in lgs:
-            nrs.softmax_topk_sample(lg, 0.9, 50, u5, token=tok5)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gs):
-        for lg in lgs:
-            nrs.softmax_topk_sample(lg, 0.9, 50, u5, token=tok5)
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(K):
-        graph.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * a.elapsed_time(b) / (K * len(lgs))
-    byts = 5 * 3072 * 2 + 5 * 8
-    lin["softmax_topk_sample_5x3072_k50_graph20"] = {
-        "mean_us": round(us, 2), "bytes": byts, "GB_s": round(byts / (us * 1e-6) / 1e9, 1),
-        "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    del lgs, graph
-    # the prefill shape: 2048 tokens x 2048 -> 4096 (qkv), bound by the matrix cores
-    lin_xp = torch.empty(2048, H, device=dev).normal_().to(torch.bfloat16)
-    lin_wp = torch.empty(4096, H, device=dev).normal_().div_(45.0).to(torch.bfloat16)
-    lin_yp = torch.empty(2048, 4096, dtype=torch.bfloat16, device=dev)
-    nxt["rmsnorm_linear_2048x2048x4096"] = (
-        lambda: nrs.rmsnorm_linear(lin_xp, lin_wp, 1e-6, out=lin_yp),
-        2048 * H * 2 + 4096 * H * 2 + 2048 * 4096 * 2)
-    for op, (fn, byts) in nxt.items():
-        for _ in range(3):
-            fn()
-        reps = []
-        for _ in range(NREP):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(K):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            reps.append(1e3 * a.elapsed_time(b) / K)
-        mean_us = sum(reps) / NREP
-        next_ops[op] = {"mean_us": round(mean_us, 2), "bytes": byts,
-                        "GB_s": round(byts / (mean_us * 1e-6) / 1e9, 1),
-                        "frac_of_peak": round(byts / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        if op.startswith("rmsnorm_linear_2048"):   # a contraction: priced against the bf16 MFMA peak
-            tf = 2 * 2048 * H * 4096 / (mean_us * 1e-6) / 1e12
-            next_ops[op] = {"mean_us": round(mean_us, 2), "TFLOP_s": round(tf, 1),
-                            "frac_of_peak": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
-                            "peak": "bf16 dense MFMA 2500 TFLOP/s"}
-    next_ops.update(lin)
-    del v, kc, vc, lg_dec, lg_big, lin_xp, lin_wp, lin_yp
-    print(f"bench: next {json.dumps(next_ops)}", file=sys.stderr, flush=True)
+    next_ops = None if args.no_next else measure_next(dev, w, ceil_cache, K)
 
     sw = per_op["swiglu"]
-    achieved = sw["GB_s"]  # algorithmic bytes per launch / mean launch duration
+    achieved = op_bytes["swiglu"] / (sw["mean_us"] * 1e-6) / 1e9  # algorithmic bytes / mean launch
     traffic = traffic_from_counters(op_bytes["swiglu"])
-    roofline = {"bound": "hbm", "kernel": "swiglu_kernel<bf16>", "achieved": achieved,
+    roofline = {"bound": "hbm", "kernel": "swiglu_kernel<bf16>", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": op_bytes["swiglu"],
-                "mean_launch_us": sw["mean_us"]}
+                "mean_launch_us": sw["mean_us"],
+                "launch_timing": "graph of 20 launches over buffer copies covering >= 1 GiB, "
+                                 "mean of 11 replays, HIP events on the replay stream",
+                "ceiling_GB_s": sw["ceiling_GB_s"], "frac_of_ceiling": sw["frac_of_ceiling"]}
 
     cpu = None
     if not args.no_cpu_baseline:
         print(f"bench: cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_tokens)
-
-    if args.sweep:
-        recs = op_sweep(dev, only=args.sweep_only)
-        with open(args.sweep, "w") as f:
-            json.dump(recs, f, indent=1)
 
     value = step_bytes / (step_ms * 1e-3) / 1e9
     out = {
@@ -531,8 +654,9 @@ def main():
                    "tokens": T, "hidden": H, "n_q_heads": nq, "n_kv_heads": nkv, "head_dim": D,
                    "intermediate": I, "sections": list(w.sections), "theta": w.theta,
                    "bytes_per_step": step_bytes, "parallelism": "single GPU"},
-        "per_op": per_op, "decode": decode, "next_ops": next_ops, "roofline": roofline,
-        "cpu_baseline": cpu,
+        "per_op": per_op, "ceilings": ceilings, "configs": configs,
+        "bar_80": bar_summary(configs) if configs else None,
+        "decode": decode, "next_ops": next_ops, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

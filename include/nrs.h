@@ -263,6 +263,24 @@ int nrs_decode_graph_create(nrs_graph *out, const nrs_decode_shape *shape,
  * same way, giving the per-node launch floor of a replay. */
 int nrs_null_graph_create(nrs_graph *out, int32_t n_nodes);
 
+/* Measurement aid (not an op): a streaming kernel that reads n_read (0-2)
+ * buffers src0, src1 and writes n_write (0-2) buffers dst0, dst1, each of
+ * `bytes` bytes, every 16-byte chunk once: one 16-byte access per thread and
+ * buffer, nontemporal loads (cached accesses when the call moves under
+ * 16 MiB in all, as the ops do).  `variant` picks one of the four patterns
+ * that streamed fastest on MI355X: bit 0 set = 256-thread workgroups (else
+ * 64), bit 1 set = stores with the sc1 + nt cache policy (else nontemporal
+ * only).  The fastest variant at an op's read/write mix and size is the
+ * practical ceiling the op is compared with.  What it writes: dst0 = src0 XOR
+ * src1 (a missing src reads as 0; a counter pattern when n_read == 0), dst1 =
+ * NOT of src0 (NOT of dst0 when n_read == 0).  With n_write == 0 nothing is
+ * written.
+ *   1 <= n_read + n_write; 0 <= variant <= 3 (NRS_ERR_ARG otherwise);
+ *   bytes >= 0, a multiple of 16; the buffers in use are 16-byte aligned and
+ *   must not overlap.  Unused pointers may be NULL. */
+int nrs_stream_probe(void *dst0, void *dst1, const void *src0, const void *src1, int32_t n_read,
+                     int32_t n_write, int64_t bytes, int32_t variant, void *stream);
+
 /* Number of kernel nodes recorded in a graph (>= 0), or a negative status. */
 int nrs_graph_node_count(nrs_graph g);
 

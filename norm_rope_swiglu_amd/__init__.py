@@ -4,8 +4,9 @@ sampling, RMSNorm fused into a Linear) as hand-written HIP kernels for gfx950 be
 (include/nrs.h), with a thin torch-tensor binding."""
 from ._native import NrsError, lib
 from .ops import (Graph, add_layernorm, add_rmsnorm, decode_graph, layernorm, mrope,
-                  mrope_kv_append, null_graph, rmsnorm, rmsnorm_linear, softmax_topk_sample, swiglu)
+                  mrope_kv_append, null_graph, rmsnorm, rmsnorm_linear, softmax_topk_sample, stream_probe,
+                  swiglu)
 
 __all__ = ["NrsError", "lib", "Graph", "add_layernorm", "add_rmsnorm", "decode_graph", "layernorm",
            "mrope", "mrope_kv_append", "null_graph", "rmsnorm", "rmsnorm_linear", "softmax_topk_sample",
-           "swiglu"]
+           "stream_probe", "swiglu"]

@@ -48,5 +48,7 @@ hipError_t launch_rmsnorm_linear(void *out, const void *x, const void *w, int64_
                                  int64_t n_in, int64_t n_out, int64_t x_stride, int64_t w_stride,
                                  int64_t out_stride, float eps, int dtype, hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);
+hipError_t launch_stream_probe(void *d0, void *d1, const void *s0, const void *s1, int n_read,
+                               int n_write, int64_t bytes, int variant, hipStream_t stream);
 
 }  // namespace nrs

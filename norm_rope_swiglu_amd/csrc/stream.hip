@@ -1,0 +1,117 @@
+// Streaming calibration kernels: the practical HBM ceilings the ops are
+// measured against.  A kernel reads n_read (0-2) buffers and writes n_write
+// (0-2) buffers of the same length, each element once, one 16-byte access
+// per thread per buffer in a one-shot grid.  Four patterns are built, the
+// ones that streamed fastest on MI355X among those measured (threads moving
+// 2, 4 or 8 chunks each copied at 5.8-6.25 TB/s against 6.6-6.7 for one):
+//   variant bit 0: 256-thread workgroups (else 64).  At 1 GiB per buffer, 64
+//     threads copy fastest (6.70 TB/s against 6.61 with 256 and 6.33 with
+//     1024) and are best for the 2-read mixes, while a read-only or
+//     write-only kernel of 64-thread groups is limited by the workgroup
+//     dispatch rate (about 4.8 TB/s against 7.0 with 256 threads);
+//   variant bit 1: stores with the sc1 + nt cache policy through a buffer
+//     resource (else nontemporal only).  At 1 GiB this wrote at 7.0 TB/s
+//     against 6.7, and copied about 1% faster; in the ops it gained at most
+//     1% on large calls and cost up to 10% on 17 MB ones, so the ops keep
+//     nontemporal stores.
+// Loads are nontemporal; calls that move under kStreamBytes in all use cached
+// accesses, as the ops do.  The ceiling of a read/write mix and size is the
+// fastest of the four.
+//
+// This is a measurement aid, not an op of the pages: it gives the copy (1
+// read, 1 write), read-only, write-only, 2-read-1-write (SwiGLU's mix) and
+// 2-read-2-write (the fused residual add's mix) rates at any size, so each
+// op's rate can be compared with kernels that do nothing but move the same
+// bytes ("Optimising autoregressive speech models", "Custom Triton kernels":
+// profile first to find the actual bottleneck).
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace nrs {
+
+namespace {
+
+constexpr int kPolicySc1Nt = 2 | 16;   // buffer-instruction cache policy bits: nt | sc1
+
+// Stores through a buffer resource based at the workgroup's first chunk (a
+// workgroup-uniform base, 32-bit offsets), so they can carry the sc1 + nt
+// policy, which a plain pointer store cannot express.
+struct out_window {
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ explicit out_window(void *base)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, 0, -1, 0x00020000)) {}
+    __device__ void store(uint32_t off, const u32x4 &v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, kPolicySc1Nt);
+    }
+};
+
+template <int NR, int NW, int BS, bool NT, bool SC1>
+__global__ __launch_bounds__(BS) void stream_kernel(u32x4 *d0, u32x4 *d1, const u32x4 *s0,
+                                                    const u32x4 *s1, int64_t n, int sink) {
+    const int64_t i0 = (int64_t)blockIdx.x * BS;
+    const int64_t i = i0 + threadIdx.x;
+    if (i >= n) return;
+    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (NR >= 1) a = load16_policy<NT>(s0 + i);
+    if (NR >= 2) b = load16_policy<NT>(s1 + i);
+    u32x4 v;
+    if (NR == 0) v = u32x4{(unsigned)i, (unsigned)(i >> 32), 0x5A5A5A5Au, 0xA5A5A5A5u};
+    else v = a ^ b;
+    if (NW == 0) {
+        // read-only: the loads feed a store that the host never enables
+        // (sink is always 0), so they are kept and nothing is written
+        if (sink) store16(d0 + i, v);
+        return;
+    }
+    const u32x4 v1 = NR >= 1 ? ~a : ~v;
+    if constexpr (NT && SC1) {
+        const uint32_t off = threadIdx.x * 16u;
+        out_window(d0 + i0).store(off, v);
+        if (NW >= 2) out_window(d1 + i0).store(off, v1);
+    } else {
+        store16_policy<NT>(d0 + i, v);
+        if (NW >= 2) store16_policy<NT>(d1 + i, v1);
+    }
+}
+
+template <int NR, int NW>
+void launch_mix(void *d0, void *d1, const void *s0, const void *s1, int64_t n, bool nt,
+                int variant, hipStream_t stream) {
+    const int bs = (variant & 1) ? 256 : 64;
+    const dim3 grid((unsigned)((n + bs - 1) / bs)), block(bs);
+#define NRS_STREAM(BS, NT, SC1)                                                                  \
+    hipLaunchKernelGGL((stream_kernel<NR, NW, BS, NT, SC1>), grid, block, 0, stream, (u32x4 *)d0, \
+                       (u32x4 *)d1, (const u32x4 *)s0, (const u32x4 *)s1, n, 0)
+    if (!nt) {
+        if (bs == 64) NRS_STREAM(64, false, false);
+        else NRS_STREAM(256, false, false);
+    } else if (variant & 2) {
+        if (bs == 64) NRS_STREAM(64, true, true);
+        else NRS_STREAM(256, true, true);
+    } else {
+        if (bs == 64) NRS_STREAM(64, true, false);
+        else NRS_STREAM(256, true, false);
+    }
+#undef NRS_STREAM
+}
+
+}  // namespace
+
+hipError_t launch_stream_probe(void *d0, void *d1, const void *s0, const void *s1, int n_read,
+                               int n_write, int64_t bytes, int variant, hipStream_t stream) {
+    const int64_t n = bytes / 16;
+    const bool nt = bytes * (n_read + n_write) >= kStreamBytes;
+    switch (n_read * 3 + n_write) {
+        case 1: launch_mix<0, 1>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 2: launch_mix<0, 2>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 3: launch_mix<1, 0>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 4: launch_mix<1, 1>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 5: launch_mix<1, 2>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 6: launch_mix<2, 0>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        case 7: launch_mix<2, 1>(d0, d1, s0, s1, n, nt, variant, stream); break;
+        default: launch_mix<2, 2>(d0, d1, s0, s1, n, nt, variant, stream); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace nrs

@@ -172,4 +172,21 @@ inline int check_topk_sample(const int32_t *token, const void *probs, const void
     return NRS_OK;
 }
 
+inline int check_stream_probe(const void *d0, const void *d1, const void *s0, const void *s1,
+                              int32_t n_read, int32_t n_write, int64_t bytes, int32_t variant) {
+    if (n_read < 0 || n_read > 2 || n_write < 0 || n_write > 2 || n_read + n_write == 0 ||
+        variant < 0 || variant > 3)
+        return NRS_ERR_ARG;
+    if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > kMaxRows * 64) return NRS_ERR_SHAPE;
+    if (bytes == 0) return NRS_OK;
+    const void *p[4] = {s0, s1, d0, d1};
+    const bool used[4] = {n_read >= 1, n_read >= 2, n_write >= 1, n_write >= 2};
+    for (int i = 0; i < 4; ++i) {
+        if (!used[i]) continue;
+        if (!p[i]) return NRS_ERR_NULL;
+        if (!aligned16(p[i])) return NRS_ERR_ALIGN;
+    }
+    return NRS_OK;
+}
+
 }  // namespace nrs

@@ -440,3 +440,24 @@ def null_graph(n_nodes: int, device=None) -> Graph:
     with torch.cuda.device(device or torch.cuda.current_device()):
         check(lib().nrs_null_graph_create(ctypes.byref(h), int(n_nodes)), "nrs_null_graph_create")
     return Graph(h.value, [])
+
+
+def stream_probe(n_read: int, n_write: int, src: list | tuple = (), dst: list | tuple = (),
+                 nbytes: int | None = None, variant: int = 0) -> None:
+    """Measurement aid: stream n_read source and n_write destination buffers
+    of nbytes bytes each (default: the first buffer's size) with the library's
+    calibration kernel, pattern `variant` 0-3 (see nrs_stream_probe in nrs.h)."""
+    bufs = list(src) + list(dst)
+    if len(src) != n_read or len(dst) != n_write or not bufs:
+        raise ValueError("give exactly n_read sources and n_write destinations")
+    if nbytes is None:
+        nbytes = bufs[0].numel() * bufs[0].element_size()
+    for t in bufs:
+        if not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+            raise ValueError("stream_probe buffers must be contiguous and hold nbytes")
+    d = _dev(*bufs)
+    ptr = lambda seq, i: seq[i].data_ptr() if i < len(seq) else None
+    with _on(d):
+        check(lib().nrs_stream_probe(ptr(dst, 0), ptr(dst, 1), ptr(src, 0), ptr(src, 1), n_read,
+                                     n_write, int(nbytes), int(variant), _stream(d)),
+              "nrs_stream_probe")

@@ -318,3 +318,29 @@ def test_graph_entry_points_reject(L):
     layers[0].post_x = None
     assert L.nrs_decode_graph_create(ctypes.byref(h), ctypes.byref(bad), layers, 1) == SECTIONS
     assert h.value is None
+
+
+# nrs_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes, variant)
+STREAM = [
+    ((P, None, P, None, 0, 0, 1024, 0), ARG),           # nothing to move
+    ((P, None, P, None, 3, 1, 1024, 0), ARG),
+    ((P, None, P, None, 1, 3, 1024, 0), ARG),
+    ((P, None, P, None, -1, 1, 1024, 0), ARG),
+    ((P, None, P, None, 1, 1, -16, 0), SHAPE),
+    ((P, None, P, None, 1, 1, 1000, 0), SHAPE),         # not whole 16-byte chunks
+    ((None, None, P, None, 1, 1, 1024, 0), NULL),
+    ((P, None, None, None, 1, 1, 1024, 0), NULL),
+    ((P, None, P, None, 2, 1, 1024, 0), NULL),          # second source missing
+    ((P, None, P, P, 2, 2, 1024, 0), NULL),             # second destination missing
+    ((U, None, P, None, 1, 1, 1024, 0), ALIGN),
+    ((P, None, U, None, 1, 1, 1024, 0), ALIGN),
+    ((P, P, P, U, 2, 2, 1024, 0), ALIGN),
+    ((None, None, None, None, 1, 1, 0, 0), OK),         # empty call: no launch
+    ((P, None, P, None, 1, 1, 1024, 4), ARG),       # no such variant
+    ((P, None, P, None, 1, 1, 1024, -1), ARG),
+]
+
+
+@pytest.mark.parametrize("args,want", STREAM)
+def test_stream_probe_rejects(L, args, want):
+    assert L.nrs_stream_probe(*args, None) == want
