@@ -22,9 +22,10 @@
 //   turns).  The (cos, sin) table lives in LDS: one evaluation per token and
 //   pair, shared by all n_q + n_kv heads of the token.
 // q and k are addressed with their own token strides, so they may sit inside
-// a packed qkv projection output.  Heads whose half is narrower than a cache
-// line take mrope_narrow_kernel below, which keeps the token blocking and the
-// table but gives consecutive lanes consecutive chunks.
+// a packed qkv projection output.  mrope_wave_kernel below gives each 64-lane
+// workgroup 64 consecutive chunks instead, one per lane, with the pair
+// partner from another lane and a per-wave table; launch_mrope picks between
+// the two by shape (measured).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -33,7 +34,7 @@ namespace nrs {
 namespace {
 constexpr double kInvTwoPi = 0.15915494309189533577;  // 1 / (2 pi), fp64
 constexpr int kMaxThreads = 1024;
-// chunks in flight per thread in mrope_narrow_kernel: two for streaming calls,
+// chunks in flight per thread in mrope_kv_narrow_kernel: two for streaming calls,
 // one for small (latency-bound) calls, which spread over more threads instead
 template <bool NT> constexpr int narrow_per_thread() { return NT ? 2 : 1; }
 }  // namespace
@@ -142,99 +143,115 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     }
 }
 
-// Heads whose half is narrower than a 128-byte cache line (1, 2 or 4 chunks
-// per half: bf16 head_dim 16, 32 or 64, fp32 8-32): consecutive lanes take
-// consecutive 16-byte chunks in memory order, so each load and store
-// instruction of a wave covers whole lines; the thread-per-pair layout above
-// would have every instruction touch only half of each line, with the other
-// half left to the next one.  In streaming calls each thread takes two
-// chunks, a block's width apart, both loads in flight together.  A chunk's pair partner (head_dim / 2
-// elements away) sits CPH lanes away in the same wave: chunk groups of a head
-// are 2 * CPH lanes, aligned, and every item count below is a multiple of
-// that, so the partner of a live item is live.  The partner's 16 bytes arrive through ds_swizzle (xor CPH within 32
-// lanes); the rotation and its rounding are those of rotate_chunks.
+// One 64-lane workgroup per 64 consecutive 16-byte chunks of q (or of k) in
+// token-major order, one chunk per lane.  Measured on MI355X, a copy moving
+// one 1 KiB piece per 64-thread workgroup, consecutive pieces going to
+// consecutive XCDs, streams faster than any pattern that hands an XCD 2 KiB
+// or more at a time (134 MB per buffer: 81% of 8 TB/s against 77%); the
+// token-blocked kernels above hand each workgroup whole tokens.  So here a
+// wave is the unit: a lane's pair partner (head_dim / 2 elements on) sits
+// CPH lanes away in the same wave and arrives by a lane swizzle (chunk
+// groups of a head are 2 * CPH lanes, aligned, since a wave starts at a
+// multiple of 64 chunks and a token holds whole heads), and the wave builds
+// the (cos, sin) entries of its own tokens in its own LDS slice, with the
+// arithmetic of build_angle_table (so the results are those of the kernels
+// above, bit for bit).  A wave's chunks never mix q and k: k's waves start
+// on a fresh wave.  Chunk indices are 32-bit: the launcher splits the tokens
+// into slabs.
 template <typename IO, bool NT, int CPH>
-__global__ __launch_bounds__(kMaxThreads) void mrope_narrow_kernel(
-    IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens, int32_t head_dim,
-    int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th, int32_t tpb,
-    int32_t q_cpt, int32_t k_cpt, fastdiv div_half, fastdiv div_q_cpt, fastdiv div_k_cpt,
-    mrope_freqs fr) {
+__global__ __launch_bounds__(64) void mrope_wave_kernel(
+    mrope_freqs fr, IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int32_t tokens,
+    int32_t half, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
+    int32_t q_cpt, int32_t k_cpt, int32_t q_waves, fastdiv div_q_cpt, fastdiv div_k_cpt,
+    fastdiv div_half) {
     constexpr int VEC = io_traits<IO>::VEC;
-    constexpr int CPHEAD = 2 * CPH;                          // chunks per head
-    constexpr int kSwz = (CPH << 10) | 0x1F;                 // bitmask mode: lane xor CPH
-    static_assert(CPH == 1 || CPH == 2 || CPH == 4, "a head's chunk group must tile a wave");
+    constexpr int CPHEAD = 2 * CPH;
+    static_assert(CPH >= 1 && CPH <= 32 && (CPH & (CPH - 1)) == 0, "chunks per half-head");
     using T = io_traits<IO>;
-    extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
-    const int half = head_dim >> 1;
-    const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;   // a multiple of 64
-    const int64_t tok0 = (int64_t)blockIdx.x * tpb;
-    const int ntok = (int)((tokens - tok0) < tpb ? (tokens - tok0) : tpb);
-    const int q_items = ntok * q_cpt;  // q chunks of the block's tokens, token-major, then k's
-    const int items = q_items + ntok * k_cpt;
+    extern __shared__ f32x2 table[];   // [tokens of this wave][half] = (cos, sin)
+    const int lane = threadIdx.x;
+    const bool is_q = (int32_t)blockIdx.x < q_waves;
+    const int32_t cpt = is_q ? q_cpt : k_cpt;
+    const fastdiv dv = is_q ? div_q_cpt : div_k_cpt;    // by value: a select, no stack copy
+    IO *const base = is_q ? q : k;
+    const int64_t stride = is_q ? q_stride : k_stride;
+    const int32_t n = tokens * cpt;                         // chunks of this tensor
+    const int32_t c0 = ((int32_t)blockIdx.x - (is_q ? 0 : q_waves)) * 64;
 
-    // item i -> its chunk's address, table slot and half
-    auto locate = [&](int i, int &tab, bool &upper) -> IO * {
-        const bool is_q = i < q_items;
-        const int j = is_q ? i : i - q_items;
-        const int tl = (int)div((uint32_t)j, is_q ? div_q_cpt : div_k_cpt);
-        const int rem = j - tl * (is_q ? q_cpt : k_cpt);    // chunk within the token's packed heads
-        const int cc = rem & (CPHEAD - 1);                   // chunk within the head
-        upper = cc >= CPH;
-        tab = tl * half + (cc & (CPH - 1)) * VEC;
-        IO *row = is_q ? q + (tok0 + tl) * q_stride : k + (tok0 + tl) * k_stride;
-        return row + (int64_t)rem * VEC;
+    // 1. the position and frequency of this lane's first (cos, sin) entry,
+    //    then this lane's chunk: the table is built while the chunk is in
+    //    flight (loads complete in order, so position loads issued after the
+    //    data would wait for it)
+    const int32_t t_first = (int32_t)div((uint32_t)c0, dv);
+    const int32_t t_last = (int32_t)div((uint32_t)min(c0 + 63, n - 1), dv);
+    const int n_ang = (t_last - t_first + 1) * half;   // entries of the wave's tokens
+    // the frequencies (fr, the first kernel argument: offset 0 of the kernel
+    // argument segment) through an opaque global pointer: read as fr.w[j],
+    // the compiler treats them as invariant and sank the first load behind
+    // the data load below; taking fr's address copied it to scratch
+    typedef const __attribute__((address_space(1))) double gdouble;
+    const void *ka = (const void *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    gdouble *const wg = (gdouble *)ka;
+    auto entry = [&](int e, int32_t &p_out, double &w_out) {
+        const int tt = (int)div((uint32_t)e, div_half);
+        const int j = e - tt * half;
+        const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
+        p_out = pos[s * pos_stride + t_first + tt];
+        w_out = wg[j];
     };
-    // every lane of the wave runs this (the swizzle reads other lanes)
-    auto rotate_store = [&](IO *p, int tab, bool upper, const u32x4 &own) {
-        u32x4 other;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            other[e] = (unsigned)__builtin_amdgcn_ds_swizzle((int)own[e], kSwz);
-        if (!p) return;
-        float a[VEC], b[VEC], o[VEC];
-        T::unpack(own, a);
-        T::unpack(other, b);
-        const f32x2 *t = table + tab;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const f32x2 cs = t[e];
-            // lower half: a cos - b sin; upper half (own = b, other = a): b cos + a sin
-            o[e] = upper ? __builtin_fmaf(a[e], cs.x, b[e] * cs.y)
-                         : __builtin_fmaf(a[e], cs.x, -(b[e] * cs.y));
-        }
-        store16_policy<NT>(p, T::pack(o));
-    };
+    int32_t p0;
+    double w0;
+    entry(lane < n_ang ? lane : 0, p0, w0);   // no branch: entry 0 always exists
+    __builtin_amdgcn_sched_barrier(0);
+    // no branch around the load (a lane past the end re-reads the last chunk
+    // and stores nothing), so the table below waits for its own loads only
+    const int32_t c = min(c0 + lane, n - 1);
+    const int32_t tl = (int32_t)div((uint32_t)c, dv);
+    const int32_t rem = c - tl * cpt;                        // chunk within the token's heads
+    const int cc = rem & (CPHEAD - 1);                       // chunk within the head
+    IO *const p = base + (int64_t)tl * stride + (int64_t)rem * VEC;
+    const u32x4 own = load16_policy<NT>(p);
+    __builtin_amdgcn_sched_barrier(0);
+    // the first entry's position and frequency are used from here on only:
+    // without this the compiler converted the position to fp64 before issuing
+    // the data load (waiting for the position load there)
+    asm volatile("" : "+v"(p0), "+v"(w0));
 
-    // rounds of U chunks per thread (a round's loads are all issued before its
-    // first rotation); the first round's loads go out before the block builds
-    // its angle table
-    constexpr int U = narrow_per_thread<NT>();
-    for (int base = 0; base < items; base += U * nthreads) {
-        IO *p[U];
-        int tab[U];
-        bool up[U];
-        u32x4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base + u * nthreads + tid;
-            p[u] = nullptr;
-            tab[u] = 0;
-            up[u] = false;
-            v[u] = u32x4{0, 0, 0, 0};
-            if (i < items) {
-                p[u] = locate(i, tab[u], up[u]);
-                v[u] = load16_policy<NT>(p[u]);
-            }
-        }
-        if (base == 0) {   // uniform: every thread takes the barrier
-            build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half,
-                              fr);
-            __syncthreads();
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) rotate_store(p[u], tab[u], up[u], v[u]);
+    // 2. the (cos, sin) entries of the wave's tokens [t_first, t_last]
+    for (int e = lane; e < n_ang; e += 64) {
+        int32_t pe = p0;
+        double we = w0;
+        if (e != lane) entry(e, pe, we);
+        const double turns = ((double)pe * we) * kInvTwoPi;
+        const float t = (float)(turns - __builtin_rint(turns));
+        table[e] = f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
     }
+    __syncthreads();   // one wave: orders its own LDS writes before the reads
+
+    // 3. the partner half-chunk from lane ^ CPH, rotate, store
+    u32x4 other;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (CPH < 32)
+            other[e] = (unsigned)__builtin_amdgcn_ds_swizzle((int)own[e], (CPH << 10) | 0x1F);
+        else
+            other[e] = (unsigned)__shfl_xor((int)own[e], 32, 64);
+    }
+    if (c0 + lane >= n) return;
+    const bool upper = cc >= CPH;
+    const f32x2 *tab = table + (tl - t_first) * half + (cc & (CPH - 1)) * VEC;
+    float a[VEC], b[VEC], o[VEC];
+    T::unpack(own, a);
+    T::unpack(other, b);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const f32x2 cs = tab[e];
+        // lower half: a cos - b sin; upper half (own = b, other = a): b cos + a sin
+        o[e] = upper ? __builtin_fmaf(a[e], cs.x, b[e] * cs.y)
+                     : __builtin_fmaf(a[e], cs.x, -(b[e] * cs.y));
+    }
+    store16_policy<NT>(p, T::pack(o));
 }
 
 // M-RoPE fused with the KV-cache append ("Optimising autoregressive speech
@@ -332,9 +349,9 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
     }
 }
 
-// The KV-cache append for half-heads under a cache line: the chunk-per-lane
-// layout of mrope_narrow_kernel (consecutive lanes, consecutive 16-byte
-// chunks; the pair partner by ds_swizzle) over the items of mrope_kv_kernel:
+// The KV-cache append for half-heads under a cache line: a chunk-per-lane
+// layout (consecutive lanes, consecutive 16-byte chunks; the pair partner by
+// ds_swizzle) over the items of mrope_kv_kernel:
 // q chunks rotated in place, k chunks rotated into the k cache, v chunks
 // copied into the v cache, in that order per block.  A token whose sequence
 // index or slot is out of range writes no cache chunk.
@@ -536,6 +553,47 @@ hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t 
     return hipGetLastError();
 }
 
+namespace {
+
+// mrope_wave_kernel over token slabs whose chunk counts fit 31 bits; heads of
+// 2 * cph chunks, cph a power of two up to 32.
+template <typename IO, bool NT>
+void launch_mrope_wave(IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
+                       int32_t n_q, int32_t n_kv, int32_t half, int cph, int64_t q_stride,
+                       int64_t k_stride, int32_t sec_t, int32_t sec_th, const mrope_freqs &fr,
+                       hipStream_t stream) {
+    const int32_t q_cpt = 2 * n_q * cph, k_cpt = 2 * n_kv * cph;
+    const int32_t max_cpt = q_cpt > k_cpt ? q_cpt : k_cpt;
+    const int32_t min_cpt = q_cpt == 0 ? k_cpt : (k_cpt == 0 ? q_cpt : (q_cpt < k_cpt ? q_cpt : k_cpt));
+    // a wave's 64 chunks touch at most 63 / cpt + 2 tokens
+    const size_t lds = (size_t)(63 / min_cpt + 2) * half * sizeof(f32x2);
+    const int64_t slab = ((int64_t)1 << 30) / max_cpt;
+    const fastdiv dq = make_fastdiv((uint32_t)(q_cpt > 0 ? q_cpt : 1)),
+                  dk = make_fastdiv((uint32_t)(k_cpt > 0 ? k_cpt : 1)),
+                  dh = make_fastdiv((uint32_t)half);
+    for (int64_t t0 = 0; t0 < tokens; t0 += slab) {
+        const int32_t nt = (int32_t)(tokens - t0 < slab ? tokens - t0 : slab);
+        const int32_t q_waves = (int32_t)(((int64_t)nt * q_cpt + 63) / 64);
+        const int32_t k_waves = (int32_t)(((int64_t)nt * k_cpt + 63) / 64);
+        const dim3 grid((unsigned)(q_waves + k_waves)), block(64);
+#define NRS_MROPE_WAVE(C)                                                                         \
+    hipLaunchKernelGGL((mrope_wave_kernel<IO, NT, C>), grid, block, lds, stream, fr,             \
+                       q + t0 * q_stride, k + t0 * k_stride, pos + t0, pos_stride, nt, half,     \
+                       q_stride, k_stride, sec_t, sec_th, q_cpt, k_cpt, q_waves, dq, dk, dh)
+        switch (cph) {
+            case 1: NRS_MROPE_WAVE(1); break;
+            case 2: NRS_MROPE_WAVE(2); break;
+            case 4: NRS_MROPE_WAVE(4); break;
+            case 8: NRS_MROPE_WAVE(8); break;
+            case 16: NRS_MROPE_WAVE(16); break;
+            default: NRS_MROPE_WAVE(32); break;
+        }
+#undef NRS_MROPE_WAVE
+    }
+}
+
+}  // namespace
+
 hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride, int64_t tokens,
                         int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t q_stride,
                         int64_t k_stride, int32_t sec_t, int32_t sec_h, const mrope_freqs &fr,
@@ -546,51 +604,25 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
     const int per_tok = (n_q + n_kv) * cph;
     const bool nt = 2 * tokens * (long long)(n_q + n_kv) * head_dim * (dtype == 0 ? 4 : 2) >=
                     kStreamBytes;
-    if (cph == 1 || cph == 2 || cph == 4) {
-        // half-heads under a cache line: mrope_narrow_kernel; streaming calls
-        // take two chunks per thread (the bytes in flight of the thread-per-pair
-        // layout below: measured at 32768 tokens, bf16 head_dim 64, 12-18%
-        // faster than one), small calls one (at 2048 tokens, H 512 and 1024,
-        // 7-13% faster than two)
-        const int cpt = 2 * per_tok;
-        const int u = nt ? narrow_per_thread<true>() : narrow_per_thread<false>();
-        int tpb = nt ? 512 * u / cpt : 1;
-        if (tpb < 1) tpb = 1;
-        for (int t = tpb; t >= 1; --t) {   // whole waves, as below
-            if ((t * cpt) % (64 * u) == 0) {
-                tpb = t;
-                break;
-            }
-        }
-        const int per_block = (tpb * cpt + u - 1) / u;
-        int threads = ((per_block + 63) / 64) * 64;
-        if (threads > kMaxThreads) threads = kMaxThreads;
-        const int64_t blocks = (tokens + tpb - 1) / tpb;
-        const size_t lds = (size_t)tpb * half * sizeof(f32x2);
-        const int q_cpt = 2 * n_q * cph, k_cpt = 2 * n_kv * cph;
-        const fastdiv dh = make_fastdiv((uint32_t)half),
-                      dq = make_fastdiv((uint32_t)(q_cpt > 0 ? q_cpt : 1)),
-                      dk = make_fastdiv((uint32_t)(k_cpt > 0 ? k_cpt : 1));
-        const dim3 grid((unsigned)blocks), block(threads);
-#define NRS_MROPE_NARROW(IO, NT, C)                                                              \
-    hipLaunchKernelGGL((mrope_narrow_kernel<IO, NT, C>), grid, block, lds, stream, (IO *)q,      \
-                       (IO *)k, pos, pos_stride, tokens, head_dim, q_stride, k_stride, sec_t,    \
-                       sec_t + sec_h, tpb, q_cpt, k_cpt, dh, dq, dk, fr)
-#define NRS_MROPE_NARROW_C(IO, NT)                                                               \
-    do {                                                                                         \
-        if (cph == 1) NRS_MROPE_NARROW(IO, NT, 1);                                               \
-        else if (cph == 2) NRS_MROPE_NARROW(IO, NT, 2);                                          \
-        else NRS_MROPE_NARROW(IO, NT, 4);                                                        \
-    } while (0)
+    // One wave per 64 chunks (mrope_wave_kernel) where its pairing works (a
+    // power-of-two number of chunks per half-head, a head within 64 lanes)
+    // and it measured faster: fp32, half-heads of 1, 2 or 4 chunks (bf16
+    // head_dim <= 64), and small calls.  Measured against the token-blocked
+    // kernels on one MI355X (graph-timed, inputs rotated past the cache, 32768
+    // tokens): fp32 head_dim 64 and 128 2-5% faster at hidden 512-4096, bf16
+    // head_dim 64 2-6% faster; the 5-token decode op set (28 layers) 169.8 ->
+    // 165.8 us per replay.  Streaming bf16 calls with head_dim 128 were 1-5%
+    // slower with it (also with two chunks per lane) and keep mrope_kernel,
+    // as do fp32 head_dim 512 and half-heads of 3, 5, 6 or 7 chunks.
+    const bool pow2 = (cph & (cph - 1)) == 0 && cph <= 32;
+    if (pow2 && (dtype == 0 || cph <= 4 || !nt)) {
         if (dtype == 0) {
-            if (nt) NRS_MROPE_NARROW_C(float, true);
-            else NRS_MROPE_NARROW_C(float, false);
+            if (nt) launch_mrope_wave<float, true>((float *)q, (float *)k, pos, pos_stride, tokens, n_q, n_kv, half, cph, q_stride, k_stride, sec_t, sec_t + sec_h, fr, stream);
+            else launch_mrope_wave<float, false>((float *)q, (float *)k, pos, pos_stride, tokens, n_q, n_kv, half, cph, q_stride, k_stride, sec_t, sec_t + sec_h, fr, stream);
         } else {
-            if (nt) NRS_MROPE_NARROW_C(__bf16, true);
-            else NRS_MROPE_NARROW_C(__bf16, false);
+            if (nt) launch_mrope_wave<__bf16, true>((__bf16 *)q, (__bf16 *)k, pos, pos_stride, tokens, n_q, n_kv, half, cph, q_stride, k_stride, sec_t, sec_t + sec_h, fr, stream);
+            else launch_mrope_wave<__bf16, false>((__bf16 *)q, (__bf16 *)k, pos, pos_stride, tokens, n_q, n_kv, half, cph, q_stride, k_stride, sec_t, sec_t + sec_h, fr, stream);
         }
-#undef NRS_MROPE_NARROW_C
-#undef NRS_MROPE_NARROW
         return hipGetLastError();
     }
     // about 512 items (threads) per block, whole tokens only; one item per

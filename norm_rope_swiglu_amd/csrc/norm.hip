@@ -48,15 +48,17 @@ template <int SEG> __device__ inline float seg_sum(float v) {
 // of two), so a 256-thread block holds 256 / SEG rows and no wave idles on a
 // short row.
 // LN selects LayerNorm (beta may be null) over RMSNorm.
-template <typename IO, int WPR, int NCH, bool ADD, bool LN, bool NT, int SEG = 64>
-__global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void norm_kernel(
+// ONE: one-wave rows one to a 64-thread block instead of four to a block.
+template <typename IO, int WPR, int NCH, bool ADD, bool LN, bool NT, int SEG = 64, bool ONE = false>
+__global__ __launch_bounds__(WPR == 1 && !ONE ? 256 : 64 * WPR) void norm_kernel(
     IO *y, IO *res_out, const IO *x, const IO *res, const IO *gamma, const IO *beta,
     int64_t rows, int32_t nchunks, int64_t x_stride, int64_t y_stride, float inv_h, float eps) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
     static_assert(SEG == 64 || (WPR == 1 && NCH == 1), "short rows take one chunk per lane");
+    static_assert(!ONE || (WPR == 1 && SEG == 64), "one row per block: one-wave rows");
     constexpr int TPR = SEG < 64 ? SEG : 64 * WPR;                     // threads per row
-    constexpr int RPB = SEG < 64 ? 256 / SEG : (WPR == 1 ? 4 : 1);     // rows per block
+    constexpr int RPB = SEG < 64 ? 256 / SEG : (WPR == 1 && !ONE ? 4 : 1);   // rows per block
     __shared__ float partial[LN ? 1 : WPR * RPB];
     __shared__ float4 moments[LN ? WPR * RPB : 1];
 
@@ -241,10 +243,22 @@ void norm_shape(int nchunks, int min_nch, int &wpr, int &nch) {
     wpr = (nchunks + 64 * nch - 1) / (64 * nch);
 }
 
+// One-wave rows of one 16-byte chunk per lane (1 KiB) in streaming calls go
+// one to a 64-thread block, the rest four to a block.  Measured on MI355X
+// (32768 rows, bf16 hidden 512, graph-timed, inputs rotated past the cache):
+// rmsnorm 12.8 -> 12.3 us, add_rmsnorm 23.1 -> 22.8 us; with 2 or 4 chunks per
+// lane, one row per block measured the same or slower.  A 64-thread block per
+// 1 KiB piece, consecutive pieces on consecutive XCDs, is the pattern that
+// copies fastest on this chip.
 template <typename IO, bool ADD, bool LN, int WPR, bool NT>
 void launch_shape(IO *y, IO *ro, const IO *x, const IO *r, const IO *g, const IO *b, int64_t rows,
                   int32_t nchunks, int nch, int64_t xs, int64_t ys, float inv_h, float eps,
                   hipStream_t stream) {
+    if (WPR == 1 && nch <= 1 && NT) {
+        hipLaunchKernelGGL((norm_kernel<IO, 1, 1, ADD, LN, NT, 64, true>), dim3((unsigned)rows),
+                           dim3(64), 0, stream, y, ro, x, r, g, b, rows, nchunks, xs, ys, inv_h, eps);
+        return;
+    }
     constexpr int RPB = WPR == 1 ? 4 : 1;
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(64 * WPR * RPB);
 #define NRS_NORM(N)                                                                             \
@@ -290,20 +304,20 @@ hipError_t launch_norm_typed(void *y, void *res_out, const void *x, const void *
     const IO *X = (const IO *)x, *R = (const IO *)res, *G = (const IO *)gamma,
              *B = (const IO *)beta;
     const bool nt = rows * hidden * (long long)sizeof(IO) * (ADD ? 4 : 2) >= kStreamBytes;
-    // Streaming-size (>= 16 MiB) calls with a residual or LayerNorm's two
-    // moments, rows of 65-256 chunks, take one wave per row and 2 or 4 chunks
-    // per thread: each wave keeps more bytes in flight and LayerNorm's
-    // moments need no cross-wave step.  Measured on MI355X (graph-timed,
-    // inputs rotated past the 256 MB cache): add_rmsnorm at 2048 x 2048 bf16
-    // 7.8 -> 7.0 us, add_layernorm 8.4 -> 7.7 us, layernorm at 32768 x 1536
-    // and x 2048 9% and 6% faster; fp32 at 2048 x 1024 12-14% faster with the
+    // Streaming-size (>= 16 MiB) calls over rows of 65-256 chunks (bf16 H =
+    // 520-2048, fp32 260-1024) take one wave per row and 2 or 4 chunks per
+    // thread: each wave keeps more bytes in flight and LayerNorm's moments
+    // need no cross-wave step.  Measured on MI355X (graph-timed, inputs
+    // rotated past the 256 MB cache): add_rmsnorm at 2048 x 2048 bf16 7.8 ->
+    // 7.0 us, add_layernorm 8.4 -> 7.7 us, layernorm at 32768 x 1536 and
+    // x 2048 9% and 6% faster; fp32 at 2048 x 1024 12-14% faster with the
     // residual, 6% for layernorm (once its 4-chunk loads lost their branch,
-    // above); 1-3% at 32768 rows.  Plain RMSNorm measured no better this way,
-    // rows of 512 chunks with 8 chunks per thread 8% slower with a residual,
-    // and small calls slower too: with it, the 5-token decode step's 28-layer
-    // op set took 183 us instead of 169 (its add_rmsnorm rows on fewer waves
-    // and CUs).
-    if ((ADD || LN) && nt && nchunks > 64 && nchunks <= 256) {
+    // above); plain rmsnorm at 32768 rows, bf16 hidden 1024 23.6 -> 22.8 us
+    // and hidden 2048 43.1 -> 42.9 us.  Rows of 512 chunks with 8 chunks per
+    // thread were 8% slower with a residual, and small calls slower too: with
+    // it, the 5-token decode step's 28-layer op set took 183 us instead of
+    // 169 (its add_rmsnorm rows on fewer waves and CUs).
+    if (nt && nchunks > 64 && nchunks <= 256) {
         wpr = 1;
         nch = nchunks <= 128 ? 2 : 4;
     }

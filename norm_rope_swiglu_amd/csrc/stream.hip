@@ -47,7 +47,7 @@ struct out_window {
 
 template <int NR, int NW, int BS, bool NT, bool SC1>
 __global__ __launch_bounds__(BS) void stream_kernel(u32x4 *d0, u32x4 *d1, const u32x4 *s0,
-                                                    const u32x4 *s1, int64_t n, int sink) {
+                                                    const u32x4 *s1, int64_t n) {
     const int64_t i0 = (int64_t)blockIdx.x * BS;
     const int64_t i = i0 + threadIdx.x;
     if (i >= n) return;
@@ -58,9 +58,11 @@ __global__ __launch_bounds__(BS) void stream_kernel(u32x4 *d0, u32x4 *d1, const 
     if (NR == 0) v = u32x4{(unsigned)i, (unsigned)(i >> 32), 0x5A5A5A5Au, 0xA5A5A5A5u};
     else v = a ^ b;
     if (NW == 0) {
-        // read-only: the loads feed a store that the host never enables
-        // (sink is always 0), so they are kept and nothing is written
-        if (sink) store16(d0 + i, v);
+        // read-only: an empty asm statement consumes the loaded values, so
+        // the loads are issued and waited for and nothing is written (a
+        // store under a never-taken branch let the compiler move the loads
+        // into that branch, and nothing was read)
+        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
         return;
     }
     const u32x4 v1 = NR >= 1 ? ~a : ~v;
@@ -81,7 +83,7 @@ void launch_mix(void *d0, void *d1, const void *s0, const void *s1, int64_t n, b
     const dim3 grid((unsigned)((n + bs - 1) / bs)), block(bs);
 #define NRS_STREAM(BS, NT, SC1)                                                                  \
     hipLaunchKernelGGL((stream_kernel<NR, NW, BS, NT, SC1>), grid, block, 0, stream, (u32x4 *)d0, \
-                       (u32x4 *)d1, (const u32x4 *)s0, (const u32x4 *)s1, n, 0)
+                       (u32x4 *)d1, (const u32x4 *)s0, (const u32x4 *)s1, n)
     if (!nt) {
         if (bs == 64) NRS_STREAM(64, false, false);
         else NRS_STREAM(256, false, false);

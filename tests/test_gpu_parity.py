@@ -329,9 +329,10 @@ def test_mrope_narrow_heads_in_packed_qkv(dt, D):
                                           (64, (8, 12, 12), 100, 40), (128, (0, 0, 64), 2, 5),
                                           (256, (32, 48, 48), 4, 2), (512, (64, 96, 96), 2, 1)])
 def test_mrope_shapes(dt, D, sec, nq, nkv):
-    # half-heads of 1, 2 or 4 chunks (bf16 D 16/32/64, fp32 D 16/32) take one thread per
-    # chunk with the partner chunk swizzled in from another lane; 140 heads of 64 give
-    # more chunks per token than a block has threads
+    # power-of-two half-heads of up to 32 chunks take one lane per chunk with the partner
+    # chunk swizzled in from another lane (waves straddling tokens where a token's heads
+    # are not whole waves); fp32 D 512 and D 48 the thread-per-pair kernel; 140 heads of
+    # 64 give more chunks per token than a block has threads
     T = 77
     q, k = _rand((T, nq, D), dt, 14), _rand((T, max(nkv, 0), D), dt, 15)
     g = torch.Generator().manual_seed(16)
