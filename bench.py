@@ -201,15 +201,16 @@ def rotation(nbytes):
     return max(1, -(-ROTATE_BYTES // max(1, nbytes)))
 
 
-def ceiling(dev, n_read, n_write, nbytes, cache, K=20, R=11):
+def ceiling(dev, n_read, n_write, nbytes, cache, K=20, R=11, row_bytes=0):
     """The calibration kernel (nrs_stream_probe) at a given read/write mix and
     size, rotated and timed exactly like the ops, fastest of its four
-    patterns; memoised in `cache`."""
+    patterns (two for row-granular copies of row_bytes rows); memoised in
+    `cache`."""
     import torch
 
     import norm_rope_swiglu_amd as nrs
 
-    key = (n_read, n_write, nbytes)
+    key = (n_read, n_write, nbytes, row_bytes)
     if key not in cache:
         nb = rotation(nbytes * (n_read + n_write))
         mk = lambda: torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -218,15 +219,17 @@ def ceiling(dev, n_read, n_write, nbytes, cache, K=20, R=11):
             src = [mk().fill_(0x11) for _ in range(n_read)]
             sets.append((src, [mk() for _ in range(n_write)]))
         best, per_variant = None, {}
-        for v in range(4):
-            t = time_graph(dev, lambda b, v=v: nrs.stream_probe(n_read, n_write, b[0], b[1], nbytes, v),
+        for v in range(2 if row_bytes else 4):
+            t = time_graph(dev, lambda b, v=v: nrs.stream_probe(n_read, n_write, b[0], b[1], nbytes, v,
+                                                                row_bytes=row_bytes),
                            sets, K, R)
             per_variant[v] = t["us"]
             if best is None or t["us"] < best["us"]:
                 best = dict(t, variant=v)
         t = best
         moved = nbytes * (n_read + n_write)
-        t.update(pattern=f"{n_read} read + {n_write} write streams of {nbytes} B",
+        t.update(pattern=f"{n_read} read + {n_write} write streams of {nbytes} B"
+                         + (f" in rows of {row_bytes} B" if row_bytes else ""),
                  GB_s=round(moved / (t["us"] * 1e-6) / 1e9, 1), buffer_sets=nb,
                  us_by_variant=per_variant)
         cache[key] = t
@@ -279,7 +282,23 @@ def measure_op(dev, op, w, ceil_cache, K=20, R=11):
     t.update(bytes=byts, GB_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
              ceiling_us=c["us"], ceiling_GB_s=c["GB_s"],
              frac_of_ceiling=round(c["us"] / t["us"], 4))
+    rb = row_ceiling_bytes(op, w.hidden, s)
+    if rb:
+        # a single-pass norm holds a row per workgroup: the ceiling of that access
+        # pattern is the row-granular copy of the same rows and mix
+        rc = ceiling(dev, nr, nw, nbytes, ceil_cache, K, R, row_bytes=rb)
+        t.update(row_ceiling_us=rc["us"], row_ceiling_GB_s=rc["GB_s"],
+                 frac_of_row_ceiling=round(rc["us"] / t["us"], 4))
     return t
+
+
+def row_ceiling_bytes(op, H, s):
+    """Row size of the row-granular calibration copy that matches a norm op
+    (0: none; the calibration kernel builds rows of 1-4, 6, 8, 12, 16 KiB)."""
+    if op not in ("rmsnorm", "add_rmsnorm", "layernorm", "add_layernorm"):
+        return 0
+    rb = H * s
+    return rb if rb % 1024 == 0 and (rb >> 10) in (1, 2, 3, 4, 6, 8, 12, 16) else 0
 
 
 def config_cases(dev):
@@ -340,9 +359,13 @@ def bar_summary(configs, bar=0.8):
             if r is None:
                 continue
             if r["frac_of_peak"] < bar:
-                below.append({"workload": rec["workload"], "op": op, "frac_of_peak": r["frac_of_peak"],
-                              "frac_of_ceiling": r["frac_of_ceiling"],
-                              "ceiling_frac_of_peak": round(r["ceiling_GB_s"] / PEAK_HBM_GBS, 4)})
+                b = {"workload": rec["workload"], "op": op, "frac_of_peak": r["frac_of_peak"],
+                     "frac_of_ceiling": r["frac_of_ceiling"],
+                     "ceiling_frac_of_peak": round(r["ceiling_GB_s"] / PEAK_HBM_GBS, 4)}
+                if "row_ceiling_GB_s" in r:
+                    b.update(frac_of_row_ceiling=r["frac_of_row_ceiling"],
+                             row_ceiling_frac_of_peak=round(r["row_ceiling_GB_s"] / PEAK_HBM_GBS, 4))
+                below.append(b)
             if worst is None or r["frac_of_ceiling"] < worst["frac_of_ceiling"]:
                 worst = {"workload": rec["workload"], "op": op, "frac_of_ceiling": r["frac_of_ceiling"]}
     n = sum(1 for rec in configs for op in ("rmsnorm", "add_rmsnorm", "mrope", "swiglu",
@@ -366,7 +389,7 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
     T, H, I, nq, nkv, D, s = w.tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2
     res = {}
 
-    def rotated(name, fn, sets, byts, mix):
+    def rotated(name, fn, sets, byts, mix, row_bytes=0):
         t = time_graph(dev, fn, sets, K, R)
         gbs = byts / (t["us"] * 1e-6) / 1e9
         t.update(bytes=byts, GB_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
@@ -374,6 +397,10 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
             c = ceiling(dev, *mix, ceil_cache, K, R)
             t.update(ceiling_us=c["us"], ceiling_GB_s=c["GB_s"],
                      frac_of_ceiling=round(c["us"] / t["us"], 4))
+        if row_bytes:
+            rc = ceiling(dev, *mix, ceil_cache, K, R, row_bytes=row_bytes)
+            t.update(row_ceiling_us=rc["us"], row_ceiling_GB_s=rc["GB_s"],
+                     frac_of_row_ceiling=round(rc["us"] / t["us"], 4))
         res[name] = t
         torch.cuda.empty_cache()
 
@@ -381,13 +408,14 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
     byts = algorithmic_bytes("layernorm", T, H, I, nq, nkv, D, s)
     sets = [(L.residual.clone(), torch.empty_like(L.x)) for _ in range(rotation(byts))]
     rotated("layernorm", lambda b: nrs.layernorm(b[0], L.gamma, beta, 1e-5, out=b[1]), sets, byts,
-            stream_mix("layernorm", T, H, I, nq, nkv, D, s))
+            stream_mix("layernorm", T, H, I, nq, nkv, D, s), row_ceiling_bytes("layernorm", H, s))
     byts = algorithmic_bytes("add_layernorm", T, H, I, nq, nkv, D, s)
     sets = [(L.x.clone(), L.residual.clone(), torch.empty_like(L.x), torch.empty_like(L.x))
             for _ in range(rotation(byts))]
     rotated("add_layernorm", lambda b: nrs.add_layernorm(b[0], b[1], L.gamma, beta, 1e-5, out=b[2],
                                                          residual_out=b[3]),
-            sets, byts, stream_mix("add_layernorm", T, H, I, nq, nkv, D, s))
+            sets, byts, stream_mix("add_layernorm", T, H, I, nq, nkv, D, s),
+            row_ceiling_bytes("add_layernorm", H, s))
     del sets
     # M-RoPE + KV-cache append: one 32768-slot sequence, slot = token index
     byts = algorithmic_bytes("mrope_kv_append", T, H, I, nq, nkv, D, s)

@@ -265,21 +265,30 @@ int nrs_null_graph_create(nrs_graph *out, int32_t n_nodes);
 
 /* Measurement aid (not an op): a streaming kernel that reads n_read (0-2)
  * buffers src0, src1 and writes n_write (0-2) buffers dst0, dst1, each of
- * `bytes` bytes, every 16-byte chunk once: one 16-byte access per thread and
- * buffer, nontemporal loads (cached accesses when the call moves under
- * 16 MiB in all, as the ops do).  `variant` picks one of the four patterns
- * that streamed fastest on MI355X: bit 0 set = 256-thread workgroups (else
- * 64), bit 1 set = stores with the sc1 + nt cache policy (else nontemporal
- * only).  The fastest variant at an op's read/write mix and size is the
- * practical ceiling the op is compared with.  What it writes: dst0 = src0 XOR
- * src1 (a missing src reads as 0; a counter pattern when n_read == 0), dst1 =
- * NOT of src0 (NOT of dst0 when n_read == 0).  With n_write == 0 nothing is
- * written.
- *   1 <= n_read + n_write; 0 <= variant <= 3 (NRS_ERR_ARG otherwise);
- *   bytes >= 0, a multiple of 16; the buffers in use are 16-byte aligned and
- *   must not overlap.  Unused pointers may be NULL. */
+ * `bytes` bytes, every 16-byte chunk once, with nontemporal loads (cached
+ * accesses when the call moves under 16 MiB in all, as the ops do).
+ *   row_bytes == 0: one 16-byte access per thread and buffer; `variant`
+ *     picks one of the four patterns that streamed fastest on MI355X: bit 0
+ *     set = 256-thread workgroups (else 64), bit 1 set = stores with the
+ *     sc1 + nt cache policy (else nontemporal only).  What it writes: dst0 =
+ *     src0 XOR src1 (a missing src reads as 0; a counter pattern when
+ *     n_read == 0), dst1 = NOT of src0 (NOT of dst0 when n_read == 0); with
+ *     n_write == 0 nothing is written.
+ *   row_bytes > 0: a row-granular copy, the access pattern of a single-pass
+ *     row reduction: whole rows of row_bytes (1, 2, 3, 4, 6, 8, 12 or 16 KiB)
+ *     per workgroup, n_read == n_write (1 or 2); variant 0 = one row per
+ *     workgroup, one chunk per thread; variant 1 = one wave per row, four
+ *     rows per 256-thread workgroup.  It writes dst0 = src0 (XOR src1),
+ *     dst1 = NOT of src0; bytes must be a whole number of rows.
+ * The fastest variant at an op's read/write mix and size is the practical
+ * ceiling the op is compared with.
+ *   1 <= n_read + n_write; 0 <= variant <= 3 (0-1 with rows), other
+ *   combinations NRS_ERR_ARG; bytes >= 0, a multiple of 16; the buffers in
+ *   use are 16-byte aligned and must not overlap.  Unused pointers may be
+ *   NULL. */
 int nrs_stream_probe(void *dst0, void *dst1, const void *src0, const void *src1, int32_t n_read,
-                     int32_t n_write, int64_t bytes, int32_t variant, void *stream);
+                     int32_t n_write, int64_t bytes, int64_t row_bytes, int32_t variant,
+                     void *stream);
 
 /* Number of kernel nodes recorded in a graph (>= 0), or a negative status. */
 int nrs_graph_node_count(nrs_graph g);

@@ -62,7 +62,7 @@ SIGNATURES = {
     "nrs_decode_graph_create": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(DecodeShape),
                                        ctypes.POINTER(DecodeLayer), _i32]),
     "nrs_null_graph_create": (_int, [ctypes.POINTER(_vp), _i32]),
-    "nrs_stream_probe": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp]),
+    "nrs_stream_probe": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _vp]),
     "nrs_graph_node_count": (_int, [_vp]),
     "nrs_graph_launch": (_int, [_vp, _vp]),
     "nrs_graph_destroy": (_int, [_vp]),

@@ -280,13 +280,14 @@ NRS_API int nrs_null_graph_create(nrs_graph *out, int32_t n_nodes) {
 }
 
 NRS_API int nrs_stream_probe(void *dst0, void *dst1, const void *src0, const void *src1,
-                             int32_t n_read, int32_t n_write, int64_t bytes, int32_t variant,
-                             void *stream) {
-    int st = nrs::check_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes, variant);
+                             int32_t n_read, int32_t n_write, int64_t bytes, int64_t row_bytes,
+                             int32_t variant, void *stream) {
+    int st = nrs::check_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes, row_bytes,
+                                     variant);
     if (st != NRS_OK || bytes == 0) return st;
     clear_stale_error();
     return hip_status(nrs::launch_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes,
-                                               variant, (hipStream_t)stream));
+                                               row_bytes, variant, (hipStream_t)stream));
 }
 
 NRS_API int nrs_graph_node_count(nrs_graph g) {

@@ -49,6 +49,7 @@ hipError_t launch_rmsnorm_linear(void *out, const void *x, const void *w, int64_
                                  int64_t out_stride, float eps, int dtype, hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);
 hipError_t launch_stream_probe(void *d0, void *d1, const void *s0, const void *s1, int n_read,
-                               int n_write, int64_t bytes, int variant, hipStream_t stream);
+                               int n_write, int64_t bytes, int64_t row_bytes, int variant,
+                               hipStream_t stream);
 
 }  // namespace nrs

@@ -16,7 +16,8 @@
 //     nontemporal stores.
 // Loads are nontemporal; calls that move under kStreamBytes in all use cached
 // accesses, as the ops do.  The ceiling of a read/write mix and size is the
-// fastest of the four.
+// fastest of the four.  With a row size, the copy is row-granular instead
+// (stream_rows_kernel): the ceiling of the norms' access pattern.
 //
 // This is a measurement aid, not an op of the pages: it gives the copy (1
 // read, 1 write), read-only, write-only, 2-read-1-write (SwiGLU's mix) and
@@ -76,6 +77,64 @@ __global__ __launch_bounds__(BS) void stream_kernel(u32x4 *d0, u32x4 *d1, const 
     }
 }
 
+// Row-granular copies: whole rows of KIB KiB per workgroup, the access
+// pattern of a single-pass row reduction (a row's elements must meet in one
+// workgroup).  WAVE = false: one row per workgroup of KIB waves, one chunk
+// per thread (the norms' layout for rows of up to 16 waves); WAVE = true: one
+// wave per row, KIB chunks per lane (lane l takes chunks l, l + 64, ...),
+// four rows to a 256-thread workgroup (the norms' layout for one-wave rows).
+template <int NR, int NW, int KIB, bool WAVE, bool NT>
+__global__ __launch_bounds__(WAVE ? 256 : 64 * KIB) void stream_rows_kernel(
+    u32x4 *d0, u32x4 *d1, const u32x4 *s0, const u32x4 *s1, int64_t rows) {
+    static_assert(NR >= 1 && NR == NW, "row copies move 1 or 2 streams each way");
+    constexpr int CPR = 64 * KIB;                       // chunks per row
+    constexpr int NCH = WAVE ? KIB : 1;                 // chunks per thread
+    const int64_t row = WAVE ? (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6) : (int64_t)blockIdx.x;
+    if (row >= rows) return;
+    const int t = WAVE ? (threadIdx.x & 63) : threadIdx.x;
+    u32x4 a[NCH], b[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t i = row * CPR + t + 64 * c;
+        a[c] = load16_policy<NT>(s0 + i);
+        if (NR >= 2) b[c] = load16_policy<NT>(s1 + i);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t i = row * CPR + t + 64 * c;
+        store16_policy<NT>(d0 + i, NR >= 2 ? a[c] ^ b[c] : a[c]);
+        if (NW >= 2) store16_policy<NT>(d1 + i, ~a[c]);
+    }
+}
+
+template <int NR, int KIB, bool NT>
+void launch_rows_kib(void *d0, void *d1, const void *s0, const void *s1, int64_t rows, bool wave,
+                     hipStream_t stream) {
+    if (wave)
+        hipLaunchKernelGGL((stream_rows_kernel<NR, NR, KIB, true, NT>), dim3((unsigned)((rows + 3) / 4)),
+                           dim3(256), 0, stream, (u32x4 *)d0, (u32x4 *)d1, (const u32x4 *)s0,
+                           (const u32x4 *)s1, rows);
+    else
+        hipLaunchKernelGGL((stream_rows_kernel<NR, NR, KIB, false, NT>), dim3((unsigned)rows),
+                           dim3(64 * KIB), 0, stream, (u32x4 *)d0, (u32x4 *)d1, (const u32x4 *)s0,
+                           (const u32x4 *)s1, rows);
+}
+
+template <int NR, bool NT>
+void launch_rows(void *d0, void *d1, const void *s0, const void *s1, int64_t rows, int kib,
+                 bool wave, hipStream_t stream) {
+    switch (kib) {
+        case 1: launch_rows_kib<NR, 1, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 2: launch_rows_kib<NR, 2, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 3: launch_rows_kib<NR, 3, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 4: launch_rows_kib<NR, 4, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 6: launch_rows_kib<NR, 6, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 8: launch_rows_kib<NR, 8, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        case 12: launch_rows_kib<NR, 12, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+        default: launch_rows_kib<NR, 16, NT>(d0, d1, s0, s1, rows, wave, stream); break;
+    }
+}
+
 template <int NR, int NW>
 void launch_mix(void *d0, void *d1, const void *s0, const void *s1, int64_t n, bool nt,
                 int variant, hipStream_t stream) {
@@ -100,9 +159,23 @@ void launch_mix(void *d0, void *d1, const void *s0, const void *s1, int64_t n, b
 }  // namespace
 
 hipError_t launch_stream_probe(void *d0, void *d1, const void *s0, const void *s1, int n_read,
-                               int n_write, int64_t bytes, int variant, hipStream_t stream) {
+                               int n_write, int64_t bytes, int64_t row_bytes, int variant,
+                               hipStream_t stream) {
     const int64_t n = bytes / 16;
     const bool nt = bytes * (n_read + n_write) >= kStreamBytes;
+    if (row_bytes > 0) {
+        const int64_t rows = bytes / row_bytes;
+        const int kib = (int)(row_bytes >> 10);
+        const bool wave = variant & 1;
+        if (n_read == 1) {
+            if (nt) launch_rows<1, true>(d0, d1, s0, s1, rows, kib, wave, stream);
+            else launch_rows<1, false>(d0, d1, s0, s1, rows, kib, wave, stream);
+        } else {
+            if (nt) launch_rows<2, true>(d0, d1, s0, s1, rows, kib, wave, stream);
+            else launch_rows<2, false>(d0, d1, s0, s1, rows, kib, wave, stream);
+        }
+        return hipGetLastError();
+    }
     switch (n_read * 3 + n_write) {
         case 1: launch_mix<0, 1>(d0, d1, s0, s1, n, nt, variant, stream); break;
         case 2: launch_mix<0, 2>(d0, d1, s0, s1, n, nt, variant, stream); break;

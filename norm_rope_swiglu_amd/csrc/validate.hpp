@@ -172,12 +172,22 @@ inline int check_topk_sample(const int32_t *token, const void *probs, const void
     return NRS_OK;
 }
 
+inline bool row_size_ok(int64_t row_bytes) {
+    const int64_t k = row_bytes >> 10;
+    return row_bytes % 1024 == 0 &&
+           (k == 1 || k == 2 || k == 3 || k == 4 || k == 6 || k == 8 || k == 12 || k == 16);
+}
+
 inline int check_stream_probe(const void *d0, const void *d1, const void *s0, const void *s1,
-                              int32_t n_read, int32_t n_write, int64_t bytes, int32_t variant) {
+                              int32_t n_read, int32_t n_write, int64_t bytes, int64_t row_bytes,
+                              int32_t variant) {
     if (n_read < 0 || n_read > 2 || n_write < 0 || n_write > 2 || n_read + n_write == 0 ||
         variant < 0 || variant > 3)
         return NRS_ERR_ARG;
+    if (row_bytes != 0 && (n_read != n_write || n_read == 0 || variant > 1)) return NRS_ERR_ARG;
     if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > kMaxRows * 64) return NRS_ERR_SHAPE;
+    if (row_bytes < 0 || (row_bytes != 0 && (!row_size_ok(row_bytes) || bytes % row_bytes != 0)))
+        return NRS_ERR_SHAPE;
     if (bytes == 0) return NRS_OK;
     const void *p[4] = {s0, s1, d0, d1};
     const bool used[4] = {n_read >= 1, n_read >= 2, n_write >= 1, n_write >= 2};

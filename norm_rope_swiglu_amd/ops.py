@@ -443,10 +443,11 @@ def null_graph(n_nodes: int, device=None) -> Graph:
 
 
 def stream_probe(n_read: int, n_write: int, src: list | tuple = (), dst: list | tuple = (),
-                 nbytes: int | None = None, variant: int = 0) -> None:
+                 nbytes: int | None = None, variant: int = 0, row_bytes: int = 0) -> None:
     """Measurement aid: stream n_read source and n_write destination buffers
     of nbytes bytes each (default: the first buffer's size) with the library's
-    calibration kernel, pattern `variant` 0-3 (see nrs_stream_probe in nrs.h)."""
+    calibration kernel, pattern `variant`; row_bytes > 0 makes it a
+    row-granular copy (see nrs_stream_probe in nrs.h)."""
     bufs = list(src) + list(dst)
     if len(src) != n_read or len(dst) != n_write or not bufs:
         raise ValueError("give exactly n_read sources and n_write destinations")
@@ -459,5 +460,6 @@ def stream_probe(n_read: int, n_write: int, src: list | tuple = (), dst: list | 
     ptr = lambda seq, i: seq[i].data_ptr() if i < len(seq) else None
     with _on(d):
         check(lib().nrs_stream_probe(ptr(dst, 0), ptr(dst, 1), ptr(src, 0), ptr(src, 1), n_read,
-                                     n_write, int(nbytes), int(variant), _stream(d)),
+                                     n_write, int(nbytes), int(row_bytes), int(variant),
+                                     _stream(d)),
               "nrs_stream_probe")

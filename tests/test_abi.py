@@ -320,24 +320,30 @@ def test_graph_entry_points_reject(L):
     assert h.value is None
 
 
-# nrs_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes, variant)
+# nrs_stream_probe(dst0, dst1, src0, src1, n_read, n_write, bytes, row_bytes, variant)
 STREAM = [
-    ((P, None, P, None, 0, 0, 1024, 0), ARG),           # nothing to move
-    ((P, None, P, None, 3, 1, 1024, 0), ARG),
-    ((P, None, P, None, 1, 3, 1024, 0), ARG),
-    ((P, None, P, None, -1, 1, 1024, 0), ARG),
-    ((P, None, P, None, 1, 1, -16, 0), SHAPE),
-    ((P, None, P, None, 1, 1, 1000, 0), SHAPE),         # not whole 16-byte chunks
-    ((None, None, P, None, 1, 1, 1024, 0), NULL),
-    ((P, None, None, None, 1, 1, 1024, 0), NULL),
-    ((P, None, P, None, 2, 1, 1024, 0), NULL),          # second source missing
-    ((P, None, P, P, 2, 2, 1024, 0), NULL),             # second destination missing
-    ((U, None, P, None, 1, 1, 1024, 0), ALIGN),
-    ((P, None, U, None, 1, 1, 1024, 0), ALIGN),
-    ((P, P, P, U, 2, 2, 1024, 0), ALIGN),
-    ((None, None, None, None, 1, 1, 0, 0), OK),         # empty call: no launch
-    ((P, None, P, None, 1, 1, 1024, 4), ARG),       # no such variant
-    ((P, None, P, None, 1, 1, 1024, -1), ARG),
+    ((P, None, P, None, 0, 0, 1024, 0, 0), ARG),           # nothing to move
+    ((P, None, P, None, 3, 1, 1024, 0, 0), ARG),
+    ((P, None, P, None, 1, 3, 1024, 0, 0), ARG),
+    ((P, None, P, None, -1, 1, 1024, 0, 0), ARG),
+    ((P, None, P, None, 1, 1, -16, 0, 0), SHAPE),
+    ((P, None, P, None, 1, 1, 1000, 0, 0), SHAPE),         # not whole 16-byte chunks
+    ((None, None, P, None, 1, 1, 1024, 0, 0), NULL),
+    ((P, None, None, None, 1, 1, 1024, 0, 0), NULL),
+    ((P, None, P, None, 2, 1, 1024, 0, 0), NULL),          # second source missing
+    ((P, None, P, P, 2, 2, 1024, 0, 0), NULL),             # second destination missing
+    ((U, None, P, None, 1, 1, 1024, 0, 0), ALIGN),
+    ((P, None, U, None, 1, 1, 1024, 0, 0), ALIGN),
+    ((P, P, P, U, 2, 2, 1024, 0, 0), ALIGN),
+    ((None, None, None, None, 1, 1, 0, 0, 0), OK),         # empty call: no launch
+    ((P, None, P, None, 1, 1, 1024, 0, 4), ARG),       # no such variant
+    ((P, None, P, None, 1, 1, 1024, 0, -1), ARG),
+    ((P, None, P, None, 1, 0, 4096, 1024, 0), ARG),   # rows move as many streams each way
+    ((P, None, P, None, 1, 1, 4096, 1024, 2), ARG),   # rows: variants 0 and 1 only
+    ((P, None, P, None, 1, 1, 4096, 1000, 0), SHAPE), # rows of whole KiB
+    ((P, None, P, None, 1, 1, 5120, 5120, 0), SHAPE), # 5 KiB rows are not built
+    ((P, None, P, None, 1, 1, 5120, 2048, 0), SHAPE), # not a whole number of rows
+    ((P, None, P, None, 1, 1, 4096, -1024, 0), SHAPE),
 ]
 
 

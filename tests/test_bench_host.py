@@ -74,3 +74,12 @@ def test_config_cases_cover_every_bandwidth_bound_workload():
     assert names[:2] == ["prefill_bf16", "ragged_bf16"]
     assert {f"sweep_{dt}_h{h}" for dt in ("bf16", "f32") for h in (512, 1024, 1536, 2048, 4096)} \
         == set(names[2:])
+
+
+def test_row_ceiling_matches_the_norm_rows():
+    assert bench.row_ceiling_bytes("rmsnorm", 2048, 2) == 4096
+    assert bench.row_ceiling_bytes("add_layernorm", 4096, 4) == 16384
+    assert bench.row_ceiling_bytes("add_rmsnorm", 1536, 2) == 3072
+    assert bench.row_ceiling_bytes("rmsnorm", 2560, 2) == 0          # 5 KiB rows are not built
+    assert bench.row_ceiling_bytes("mrope", 2048, 2) == 0
+    assert bench.row_ceiling_bytes("swiglu", 2048, 2) == 0

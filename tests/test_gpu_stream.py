@@ -54,6 +54,22 @@ def test_stream_probe_outputs(nbytes, n_read, n_write, variant):
         assert torch.equal(d.cpu(), s)
 
 
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("kib,rows", [(1, 5), (2, 3), (3, 9), (4, 7), (6, 2), (8, 5), (12, 1),
+                                      (16, 6), (4, 4096 + 3)])
+@pytest.mark.parametrize("n", [1, 2])
+def test_stream_probe_rows(kib, rows, n, variant):
+    nbytes = rows * kib * 1024
+    src = [_words(nbytes, 20 + i) for i in range(n)]
+    ddst = [torch.full((nbytes // 4,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
+            for _ in range(n)]
+    nrs.stream_probe(n, n, [t.cuda() for t in src], ddst, nbytes, variant, row_bytes=kib * 1024)
+    torch.cuda.synchronize()
+    assert torch.equal(ddst[0].cpu(), src[0] if n == 1 else src[0] ^ src[1])
+    if n == 2:
+        assert torch.equal(ddst[1].cpu(), ~src[0])
+
+
 def test_stream_probe_empty_call():
     nrs.stream_probe(1, 1, [torch.empty(16, dtype=torch.uint8, device="cuda")],
                      [torch.empty(16, dtype=torch.uint8, device="cuda")], 0)
