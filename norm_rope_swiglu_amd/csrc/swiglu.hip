@@ -5,12 +5,15 @@
 // row holds [gate | up], `inter` elements each; out rows hold `inter`.
 //
 // Elementwise streaming: one thread per 16-byte output chunk, reading the
-// matching gate and up chunks; measured on MI355X, one access per thread per
-// stream in a one-shot grid streams faster than threads that loop over
-// several chunks.  Each XCD takes one contiguous eighth of the chunks
-// (measured ~1.6% faster than the round-robin interleave; the norms and
-// M-RoPE measured faster interleaved).  Chunk -> (row, column) uses a
-// multiply-high division by the fixed chunks-per-row.
+// matching gate and up chunks, in 64-thread workgroups taken in order (so
+// consecutive 1 KiB pieces of the output go to consecutive XCDs); measured on
+// MI355X, one access per thread per stream in a one-shot grid streams faster
+// than threads that loop over several chunks, and 64-thread workgroups in
+// order beat 256-thread ones with each XCD walking one contiguous eighth of
+// the chunks by 3-7% (graph-timed, inputs rotated past the cache: 32768 x 6144
+// bf16 184.0 -> 178.7 us, 2048 x 6144 14.6 -> 13.7 us, 32768 x 1536 48.3 ->
+// 46.8 us; 128- and 512-thread workgroups fell in between).  Chunk -> (row,
+// column) uses a multiply-high division by the fixed chunks-per-row.
 //
 // Numerics: sigmoid(g) = 1/(1 + e^-g) is safe while e^-g stays finite
 // (g >= -80).  Below that, silu(g) * up can still be a normal fp32 number
@@ -25,8 +28,7 @@
 namespace nrs {
 
 namespace {
-constexpr int kThreads = 256;
-constexpr int kSmallThreads = 64;   // block size of calls below kStreamBytes
+constexpr int kThreads = 64;
 constexpr float kExpM64 = 1.60381089054863785e-28f;  // e^-64
 
 __device__ inline float silu_mul_tail(float g, float u) {
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(IO *out, const IO *gat
                                                           int64_t gu_stride, int64_t out_stride) {
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    const int32_t ci = (int32_t)xcd_contiguous(blockIdx.x, gridDim.x) * (int32_t)blockDim.x + threadIdx.x;
+    const int32_t ci = (int32_t)blockIdx.x * kThreads + threadIdx.x;
     if (ci >= total) return;
     const int32_t r = (int32_t)div((uint32_t)ci, div_cpr);
     const int32_t col = ci - r * cpr;
@@ -76,15 +78,14 @@ hipError_t launch_swiglu(void *out, const void *gate_up, int64_t rows, int64_t i
         const int64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
         const int32_t total = (int32_t)(nr * cpr);
         const bool nt = 3 * nr * inter * (long long)esz >= kStreamBytes;
-        // small calls are latency-bound: narrow blocks spread them over more
-        // CUs (measured at the 5-token decode step: 64-thread blocks shorten
-        // the kernel by ~0.07 us; more chunks per thread lengthen it)
-        const int bt = nt ? kThreads : kSmallThreads;
-        const int64_t blocks = (total + bt - 1) / bt;
+        // (small calls are latency-bound and take the same narrow blocks,
+        // which spread them over more CUs: measured at the 5-token decode
+        // step, 64-thread blocks shorten the kernel by ~0.07 us against 256)
+        const int64_t blocks = (total + kThreads - 1) / kThreads;
         const fastdiv dv = make_fastdiv((uint32_t)cpr);
         const char *gu = (const char *)gate_up + r0 * gu_stride * esz;
         char *o = (char *)out + r0 * out_stride * esz;
-        const dim3 grid((unsigned)blocks), block(bt);
+        const dim3 grid((unsigned)blocks), block(kThreads);
 #define NRS_SWIGLU(IO, NT)                                                                        \
     hipLaunchKernelGGL((swiglu_kernel<IO, NT>), grid, block, 0, stream, (IO *)o, (const IO *)gu, \
                        total, (int32_t)cpr, dv, inter, gu_stride, out_stride)
