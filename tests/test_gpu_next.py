@@ -172,13 +172,19 @@ def _u(rows, seed):
     return W.uniform(W.stream_key(seed, f"u/{rows}"), rows).to(torch.float32)
 
 
-def sample_parity(logits, T, k, u, tag):
-    """Check the full softmax, and that every sampled token lies in the
-    oracle's kept set with u inside its exact CDF interval (to DELTA); where u
-    is farther than DELTA from every boundary the token must be the oracle's."""
-    tok, probs = nrs.softmax_topk_sample(logits.cuda(), T, k, u.cuda(), probs=True)
-    otok, oprobs, kept, cdf = oracle.softmax_topk_sample(logits, T, k, u.numpy())
-    check(f"{tag}/probs", probs, oprobs)
+def sample_parity(logits, T, k, u, tag, want_probs=True):
+    """Check the full softmax (when asked for), and that every sampled token
+    lies in the oracle's kept set with u inside its exact CDF interval (to
+    DELTA); where u is farther than DELTA from every boundary the token must be
+    the oracle's."""
+    if want_probs:
+        tok, probs = nrs.softmax_topk_sample(logits.cuda(), T, k, u.cuda(), probs=True)
+    else:
+        tok = nrs.softmax_topk_sample(logits.cuda(), T, k, u.cuda())
+    otok, oprobs, kept, cdf = oracle.softmax_topk_sample(logits, T, k, u.numpy(),
+                                                         want_probs=want_probs)
+    if want_probs:
+        check(f"{tag}/probs", probs, oprobs)
     tok = tok.cpu().numpy()
     uu = u.numpy().astype(np.float64)
     for r in range(logits.shape[0]):
@@ -251,6 +257,52 @@ def test_sample_ties(dt):
     tok, _ = sample_parity(lg, 1.0, 20, torch.tensor([0.0, 0.9999, 0.97], dtype=torch.float32),
                            f"sample/many_ties/{dt}")
     assert tok[0] == 5000
+
+
+@pytest.mark.parametrize("dt,vocab,k,rows", [("bf16", 151936, 50, 7), ("bf16", 151936, 200, 3),
+                                             ("bf16", 151936, 1024, 2), ("bf16", 65544, 64, 5),
+                                             ("bf16", 70000, 7, 257), ("f32", 40000, 64, 6),
+                                             ("f32", 32776, 1, 4), ("f32", 151936, 33, 3)])
+def test_sample_long_rows_token_only(dt, vocab, k, rows):
+    # rows longer than a workgroup holds in registers, sampled without the softmax output
+    lg = _logits(rows, vocab, 3.0, dt, 41)
+    sample_parity(lg, 0.9, k, _u(rows, 42), f"sample/long/{dt}/V{vocab}/k{k}", want_probs=False)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_ties(dt):
+    # ties in a streamed row, and equal maxima at scattered places (each 65536 logits apart
+    # in bf16, 32768 in fp32: a register-held row's length)
+    V = 151936
+    seg = 65536 if dt == "bf16" else 32768
+    n_seg = -(-V // seg)
+    # integer-valued rows: many ties at the k-th value
+    lg = _logits(5, V, 2.0, dt, 43, ties=True)
+    sample_parity(lg, 1.0, 100, _u(5, 44), f"sample/long_ties/{dt}", want_probs=False)
+    # equal maxima around every multiple of that length, fewer than k of them above a flat
+    # row: the kept set is every maximum plus the lowest-index zeros
+    lg = torch.zeros(4, V)
+    for b in range(1, n_seg):
+        lg[:, b * seg - 3: b * seg + 3] = 5.0
+    lg[:, V - 2:] = 5.0
+    lg = lg.to(W.store(torch.zeros(1), dt).dtype)
+    u = torch.tensor([0.0, 0.3, 0.7, 0.999999], dtype=torch.float32)
+    tok, otok = sample_parity(lg, 1.0, 64, u, f"sample/long_scattered_max/{dt}", want_probs=False)
+    assert tok[0] == seg - 3                                # the lowest-index maximum first
+    # all equal: the lowest indices are kept
+    lg = torch.zeros(3, V).to(lg.dtype)
+    tok, _ = sample_parity(lg, 1.0, 16, torch.tensor([0.0, 0.5, 0.99], dtype=torch.float32),
+                           f"sample/long_flat/{dt}", want_probs=False)
+    assert tok.tolist() == [0, 8, 15]
+
+
+def test_sample_long_rows_greedy_tied_maximum():
+    lg = _logits(8, 151936, 4.0, "bf16", 45).float()
+    top = lg.max(dim=1).values + 2.0
+    lg[:, 120000] = top
+    lg[:, 140000] = top                                    # tied maximum: lower index wins
+    tok = nrs.softmax_topk_sample(lg.to(torch.bfloat16).cuda(), 1.0, 1, _u(8, 46).cuda()).cpu()
+    assert torch.all(tok == 120000)
 
 
 def test_sample_greedy_is_first_argmax():
