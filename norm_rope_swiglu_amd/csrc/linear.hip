@@ -313,16 +313,32 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
 // separate arrays.  The compiler then orders each fragment read only after
 // the loads into its own slot.
 
-// 16-byte chunk c of tile row `row` in a stage slot whose rows are CPR chunks
-// long: the chunk is stored at slot c ^ swizzle(row), which spreads both a
-// fragment read (16 consecutive rows, one chunk) and a 1 KiB load over every
-// bank.
+// Where a tile row's 16-byte chunks sit in a stage slot whose rows are CPR
+// chunks long.  A fragment read takes one chunk from each of 16 consecutive
+// tile rows (g = lane / 16 picks the chunk); a 1 KiB load fills 1 KiB of LDS
+// in lane order.  Both must spread over every bank.  128-byte rows (CPR 8)
+// keep the tile's row order and store chunk c at slot c ^ ((row / 2) % 8).
+// With 64-byte rows (CPR 4) an in-row swizzle alone left every fragment read
+// two-way conflicted on MI355X (SQ_LDS_BANK_CONFLICT: four cycles on each
+// ds_read_b128, against none with 128-byte rows): within an aligned block of
+// 16 rows, the LDS row of tile row r is gemm_pos(r), which gives the rows that
+// a read serves together different 64-byte quarters of a 256-byte bank line,
+// and chunk c sits at slot c ^ ((r / 2) % 4).
 template <int CPR> __device__ inline int gemm_swizzle(int row) {
     if constexpr (CPR == 8) return (row >> 1) & 7;
-    else return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+    else return (row >> 1) & 3;
+}
+// LDS row, within its aligned block of 16, of tile row r (0..15), and back
+template <int CPR> __device__ inline int gemm_pos(int r) {
+    if constexpr (CPR == 8) return r;
+    else return (r & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 3) << 2);
+}
+template <int CPR> __device__ inline int gemm_row_of(int p) {
+    if constexpr (CPR == 8) return p;
+    else return (p & 1) | (((p >> 2) & 3) << 1) | (((p >> 1) & 1) << 3);
 }
 template <int CPR> __device__ inline int gemm_at(int row, int c) {
-    return row * CPR * 8 + ((c ^ gemm_swizzle<CPR>(row)) << 3);
+    return ((row & ~15) + gemm_pos<CPR>(row & 15)) * CPR * 8 + ((c ^ gemm_swizzle<CPR>(row)) << 3);
 }
 
 // s_waitcnt with vmcnt = N and the other counters at their maximum
@@ -361,6 +377,7 @@ __global__ __launch_bounds__(512, 1) void rmsnorm_linear_gemm_kernel(
     constexpr int NA = (BM / 2) / RPK / 4, NB = (BN / 2) / RPK / 4;   // loads per wave per stage
     constexpr int NL = NA + NB;
     static_assert(NA * RPK * 4 == BM / 2 && NB * RPK * 4 == BN / 2, "loads split evenly");
+    static_assert(CPR == 8 || RPK == 16, "64-byte rows: loads cover whole 16-row blocks");
     constexpr int D = 2;                                  // stages in flight ahead of the one read
     __shared__ __attribute__((aligned(16))) __bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK];
     __shared__ __attribute__((aligned(16))) __bf16 B0[BN * BK], B1[BN * BK], B2[BN * BK];
@@ -392,19 +409,21 @@ __global__ __launch_bounds__(512, 1) void rmsnorm_linear_gemm_kernel(
     constexpr uint32_t kOut = 0x80000000u;    // beyond any buffer here: reads as zeros
 
     // this wave's loads.  Load j covers RPK tile rows; lane l fills LDS slot l
-    // of that 1 KiB block, i.e. row base + l / CPR, stored chunk l % CPR,
-    // which holds input chunk (l % CPR) ^ swizzle(row).
+    // of that 1 KiB block, i.e. LDS row base + l / CPR, stored chunk l % CPR,
+    // which holds tile row lr = base + gemm_row_of(l / CPR) (a load starts on
+    // a 16-row boundary, or covers 8 rows of 128 bytes) and its input chunk
+    // (l % CPR) ^ swizzle(lr).
     uint32_t offa[NA], offb[NB];
     int cla[NA], clb[NB];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-        const int lr = grp * (BM / 2) + (wig * NA + j) * RPK + lane / CPR;
+        const int lr = grp * (BM / 2) + (wig * NA + j) * RPK + gemm_row_of<CPR>(lane / CPR);
         cla[j] = ((lane % CPR) ^ gemm_swizzle<CPR>(lr)) * 8;
         offa[j] = (uint32_t)(lr * (int)x_stride + cla[j]) * 2u;
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        const int lr = grp * (BN / 2) + (wig * NB + j) * RPK + lane / CPR;
+        const int lr = grp * (BN / 2) + (wig * NB + j) * RPK + gemm_row_of<CPR>(lane / CPR);
         clb[j] = ((lane % CPR) ^ gemm_swizzle<CPR>(lr)) * 8;
         offb[j] = (uint32_t)(lr * (int)w_stride + clb[j]) * 2u;
     }
