@@ -374,6 +374,24 @@ def bar_summary(configs, bar=0.8):
             "lowest_frac_of_ceiling": worst}
 
 
+def eager_time(dev, fn, K):
+    """Mean microseconds of fn over K launches queued back to back after three
+    warm-up calls, bracketed by events on the current stream."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    for _ in range(K):
+        fn()
+    b.record(cur)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / K
+
+
 def measure_next(dev, w, ceil_cache, K=20, R=11):
     """The ops built beside the four-op step, on the step's batch shapes:
     LayerNorm (plain and fused), M-RoPE + KV-cache append and the sampler over
@@ -504,8 +522,16 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
         tf = 2 * M * H * N / (t["mean_us"] * 1e-6) / 1e12
         t.update(TFLOP_s=round(tf, 1), frac_of_peak=round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
                  peak="bf16 dense MFMA 2500 TFLOP/s")
+        # the vendor library's plain product of the same operands (no norm), for a
+        # practical ceiling: torch.mm on a contiguous W^T, launched eagerly (a library
+        # call may record memsets, which stay out of graphs)
+        wt = wp.t().contiguous()
+        lib_us = eager_time(dev, lambda: torch.mm(xp, wt, out=yp), K)
+        ltf = 2 * M * H * N / (lib_us * 1e-6) / 1e12
+        t.update(library_us=round(lib_us, 2), library_TFLOP_s=round(ltf, 1),
+                 frac_of_library=round(lib_us / t["mean_us"], 4), library="torch.mm (hipBLASLt)")
         res[f"rmsnorm_linear_{M}x{H}x{N}"] = t
-        del xp, wp, yp
+        del xp, wp, yp, wt
     torch.cuda.empty_cache()
     print(f"bench: next {json.dumps(res)}", file=sys.stderr, flush=True)
     return res

@@ -157,6 +157,17 @@ def test_gemm_big_tiles_with_tails():
     lin_parity(x, w, 1e-6, "lin/gemm/big4100", rows=rows)
 
 
+@pytest.mark.parametrize("n_in", [8, 40, 72, 104, 168, 232, 264])
+def test_gemm_big_tiles_short_inputs(n_in):
+    # the large-tile path with 1-9 stages of 32 inputs: fewer stages than the
+    # ring's prologue fills, the tail alone, and one steady pass before it
+    x, w = lin_inputs(4096, n_in, 4096, "bf16", 16)
+    g = torch.Generator().manual_seed(17)
+    rows = torch.unique(torch.cat([torch.tensor([0, 255, 256, 4095]),
+                                   torch.randint(0, 4096, (12,), generator=g)]))
+    lin_parity(x, w, 1e-6, f"lin/gemm/big_short{n_in}", rows=rows)
+
+
 def test_gemm_strided_operands():
     xb, wb = lin_inputs(200, 640, 96, "bf16", 11)
     lin_parity(xb[:, 64:576], wb[:, 128:640], 1e-6, "lin/gemm/strided")
