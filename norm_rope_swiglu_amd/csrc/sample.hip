@@ -30,9 +30,16 @@
 //      prefix exceeds u * total.
 // Rows of up to 8 16-byte chunks per thread (65536 bf16 or 32768 fp32
 // logits) are read from HBM once, into registers, as order keys, and every
-// pass runs over the registers; longer rows are re-read (from the caches) by
-// each pass.  (At 20 chunks per thread the registers spill and the kernel
-// ran slower than streaming the row.)
+// pass runs over the registers.  (At 20 chunks per thread the registers spill
+// and the kernel ran slower than streaming the row.)  Longer rows, when only
+// the token is asked for, are read once too: the first 8 chunks per thread
+// are held, the top_k-th largest of the threads' maxima (a lower bound for
+// the row's top_k-th largest) is selected, and one pass over the held keys and
+// the streamed rest keeps every logit at or above it (about 2.5 top_k of
+// them), which step 3 sorts.  Such a row falls back to the passes above,
+// re-reading it, only when the kept logits overflow the 1024-entry buffer
+// (top_k near 1024, or a row whose logits rise along it), or when the softmax
+// output is asked for.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -83,7 +90,16 @@ template <> struct keys<float> {
         return k;
     }
     __device__ static inline uint32_t at(const u32x4 &k, int e) { return k[e]; }
+    // the largest full key of a chunk
+    __device__ static inline uint32_t chunk_max(const u32x4 &k) {
+        const uint32_t a = k[0] > k[1] ? k[0] : k[1], b = k[2] > k[3] ? k[2] : k[3];
+        return a > b ? a : b;
+    }
+    __device__ static inline uint32_t max2(uint32_t a, uint32_t b) { return a > b ? a : b; }
+    __device__ static inline uint32_t full(uint32_t m) { return m; }
 };
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 template <> struct keys<__bf16> {
     static constexpr int VEC = 8;
@@ -101,6 +117,20 @@ template <> struct keys<__bf16> {
     __device__ static inline uint32_t at(const u32x4 &k, int e) {
         const uint32_t h = (k[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
         return (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);   // the full fp32 key
+    }
+    // per-half maxima of two words of keys, and the largest 16-bit key of a
+    // chunk (as its full key by full())
+    __device__ static inline uint32_t max2(uint32_t a, uint32_t b) {
+        const us2 m = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
+        return __builtin_bit_cast(uint32_t, m);
+    }
+    __device__ static inline uint32_t chunk_max(const u32x4 &k) {
+        const uint32_t w = max2(max2(k[0], k[1]), max2(k[2], k[3]));
+        return full(w);
+    }
+    __device__ static inline uint32_t full(uint32_t w) {
+        const uint32_t lo = w & 0xFFFFu, hi = w >> 16, h = lo > hi ? lo : hi;
+        return (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
     }
 };
 
@@ -135,66 +165,112 @@ __device__ inline float block_inclusive_scan(float v, float *wave_tot) {
 }
 }  // namespace
 
-// CPT > 0: thread t holds the row's chunks t, t + 1024, ... (at most CPT of
-// them) in registers; CPT == 0: every pass streams the row from memory.
+// The workgroup's LDS, shared by a row's first attempt and its fallback.
+struct SampleShared {
+    // bin-major: the replicas of a bin sit on kRep consecutive banks
+    uint32_t hist[kHistWords];
+    uint32_t wtot[4];
+    uint32_t sel[3];            // selected digit, count above it, count equal
+    int iscan[kWaves];
+    float fscan[kWaves];
+    alignas(16) uint32_t ckey[kThreads];   // kept entries: key, index
+    alignas(16) int32_t cidx[kThreads];
+    float csum[kThreads];       // prefix sums of the kept weights
+    int32_t rank_of[kThreads];  // ranks of the kept entries (up to kRankMax)
+    uint32_t n_gt;
+    int32_t pick;
+};
+
+// One row.  CPT > 0: thread t holds the row's chunks t, t + 1024, ... (at
+// most CPT of them) in registers; CPT == 0: every pass streams the row from
+// memory.  CPT < 0 (rows longer than -CPT chunks per thread, token only):
+// the row's first -CPT * 1024 chunks are held and selected as a row of their
+// own; their k-th largest key is a lower bound for the whole row's, so one
+// pass over the rest of the row appends every key at or above it to the kept
+// entries, and the sort of all of them gives the row's top k.  The row is read
+// once.  If the kept entries overflow the buffer (a row whose later logits
+// run higher, for instance), it returns false having written nothing, and the
+// row is then selected again as CPT == 0.  Otherwise it returns true.
 template <typename IO, int CPT>
-__global__ __launch_bounds__(kThreads) void topk_sample_kernel(
-    int32_t *token, IO *probs, const IO *logits, int64_t vocab, int64_t row_stride,
-    int64_t probs_stride, float inv_temp, int32_t top_k, const float *u) {
+__device__ __attribute__((always_inline)) bool sample_row(
+    SampleShared &sh, int32_t *token, IO *probs, const IO *logits, int64_t vocab,
+    int64_t row_stride, int64_t probs_stride, float inv_temp, int32_t top_k, const float *u) {
     using K = keys<IO>;
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
-    constexpr int kDigitBits = CPT > 0 ? 8 : 12;
-    constexpr int kRep = CPT == 1 ? 8 : (CPT > 0 ? 32 : 4);
+    constexpr bool FILTER = CPT < 0;
+    constexpr int HC = FILTER ? -CPT : CPT;   // chunks held per thread
+    constexpr int kDigitBits = HC > 0 ? 8 : 12;
+    constexpr int kRep = HC == 1 ? 8 : (HC > 0 ? 32 : 4);
     static_assert((kRep << kDigitBits) <= kHistWords, "histogram fits");
-    // bin-major: the replicas of a bin sit on kRep consecutive banks
-    __shared__ uint32_t hist[kHistWords];
-    __shared__ uint32_t wtot[4];
-    __shared__ uint32_t sel[3];            // selected digit, count above it, count equal
-    __shared__ int iscan[kWaves];
-    __shared__ float fscan[kWaves];
-    __shared__ __attribute__((aligned(16))) uint32_t ckey[kThreads];   // kept entries: key, index
-    __shared__ __attribute__((aligned(16))) int32_t cidx[kThreads];
-    __shared__ float csum[kThreads];       // prefix sums of the kept weights
-    __shared__ int32_t rank_of[kThreads];  // ranks of the kept entries (up to kRankMax)
-    __shared__ uint32_t n_gt;
-    __shared__ int32_t pick;
+    uint32_t *hist = sh.hist, *wtot = sh.wtot, *sel = sh.sel, *ckey = sh.ckey;
+    int *iscan = sh.iscan;
+    float *fscan = sh.fscan, *csum = sh.csum;
+    int32_t *cidx = sh.cidx, *rank_of = sh.rank_of;
+    uint32_t &n_gt = sh.n_gt;
+    int32_t &pick = sh.pick;
 
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const IO *x = logits + row * row_stride;
     const int64_t nchunks = vocab / VEC;
+    // chunks the select and gather run over: the whole row, or its held part
+    const int64_t nheld = FILTER ? (nchunks < (int64_t)HC * kThreads ? nchunks : (int64_t)HC * kThreads)
+                                 : nchunks;
 
     // the row's source: keys in registers (loaded here, all at once) or
     // memory (converted to keys as each pass reads it)
-    u32x4 held[CPT > 0 ? CPT : 1];
-    if constexpr (CPT > 0) {
+    u32x4 held[HC > 0 ? HC : 1];
+    // FILTER: the rest of the row streams in batches of kUnroll chunks per
+    // thread, the next batch in flight while one is filtered; the first batch
+    // is issued with the held part.  These loads take no branch (an index past
+    // the row reads its last chunk, skipped by the filter), so the compiler
+    // waits for each batch alone rather than for every load in flight.
+    // Measured on MI355X (256 x 151936 bf16): issuing a second batch with the
+    // held part, or the first three batches as straight-line code, made the
+    // call 7% slower (the held part, which the select waits for, then lands
+    // later).
+    u32x4 sa[FILTER ? kUnroll : 1], sb[FILTER ? kUnroll : 1];
+    auto load_batch = [&](u32x4 (&buf)[FILTER ? kUnroll : 1], int64_t c0) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int64_t c = tid + (int64_t)j * kThreads;
-            if (c < nchunks) held[j] = load16(x + c * VEC);
+        for (int j = 0; j < (FILTER ? kUnroll : 1); ++j) {
+            const int64_t c = c0 + (int64_t)j * kThreads;
+            buf[j] = load16(x + (c < nchunks ? c : nchunks - 1) * VEC);
         }
+    };
+    if constexpr (FILTER) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) held[j] = K::from_raw(held[j]);
+        for (int j = 0; j < HC; ++j) held[j] = load16(x + (tid + (int64_t)j * kThreads) * VEC);
+        load_batch(sa, nheld + tid);
+    } else if constexpr (HC > 0) {
+#pragma unroll
+        for (int j = 0; j < HC; ++j) {
+            const int64_t c = tid + (int64_t)j * kThreads;
+            if (c < nheld) held[j] = load16(x + c * VEC);
+        }
+    }
+    if constexpr (HC > 0) {
+#pragma unroll
+        for (int j = 0; j < HC; ++j) held[j] = K::from_raw(held[j]);
     }
     // Marks the held keys as rewritten (an empty asm statement that emits no
     // instruction), so each pass re-derives per-element keys from them instead
     // of the compiler keeping every pass's unpacked keys alive in registers.
     auto opaque = [&]() {
-        if constexpr (CPT > 0) {
+        if constexpr (HC > 0) {
 #pragma unroll
-            for (int j = 0; j < CPT; ++j)
+            for (int j = 0; j < HC; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(held[j][i]));
         }
     };
     // f(c, keys) for every chunk c this thread owns, in increasing c
     auto for_chunks = [&](auto &&f) {
-        if constexpr (CPT > 0) {
+        if constexpr (HC > 0) {
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
+            for (int j = 0; j < HC; ++j) {
                 const int64_t c = tid + (int64_t)j * kThreads;
-                if (c < nchunks) f(c, held[j]);
+                if (c < nheld) f(c, held[j]);
             }
         } else {
             for (int64_t c0 = tid; c0 < nchunks; c0 += kUnroll * kThreads) {
@@ -223,6 +299,21 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     //    histograms keep replicas (indexed by lane) so lanes counting the same
     //    bin, common with peaky logits, split over several addresses.
     constexpr int kKeyBits = sizeof(IO) == 4 ? 32 : 16;   // bits that vary in a key
+    // FILTER: the select runs over one key per thread, the largest it holds.
+    // These are distinct entries of the row, so the top_k-th largest of them
+    // is at most the row's top_k-th largest: every kept entry lies at or
+    // above it.  With top_k well below the thread count, the row's largest
+    // entries mostly sit in different threads, and the bound is nearly the
+    // row's own top_k-th largest.
+    uint32_t mkey = 0;
+    if constexpr (FILTER) {
+        uint32_t w = 0;
+        for_chunks([&](int64_t, const u32x4 &kc) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w = K::max2(w, kc[i]);
+        });
+        mkey = K::full(w);
+    }
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)top_k;
     const uint32_t rep = tid & (kRep - 1);
@@ -238,14 +329,18 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         for (int i = tid; i < (int)nb * kRep; i += kThreads) hist[i] = 0;
         opaque();
         __syncthreads();
-        for_chunks([&](int64_t, const u32x4 &kc) {
+        if constexpr (FILTER) {
+            if ((mkey & pmask) == prefix) atomicAdd(&hist[((mkey >> shift) & (nb - 1)) * kRep + rep], 1u);
+        } else {
+            for_chunks([&](int64_t, const u32x4 &kc) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint32_t key = K::at(kc, e);
-                if ((key & pmask) == prefix)
-                    atomicAdd(&hist[((key >> shift) & (nb - 1)) * kRep + rep], 1u);
-            }
-        });
+                for (int e = 0; e < VEC; ++e) {
+                    const uint32_t key = K::at(kc, e);
+                    if ((key & pmask) == prefix)
+                        atomicAdd(&hist[((key >> shift) & (nb - 1)) * kRep + rep], 1u);
+                }
+            });
+        }
         __syncthreads();
         if (nb <= 256) {
             // thread t < nb sums digit nb-1-t (rotating the replica index keeps
@@ -312,7 +407,10 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         const int cand = (top_k - (int)need) + (int)sel[2];
         const bool last = shift == 32 - kKeyBits;
         fits = cand <= kThreads;
-        const bool stop = last || cand <= kRankMax || (CPT == 0 && fits);
+        // the bound from the threads' maxima filters the whole row: it stops
+        // only once few keys beyond the k needed share the selected bin
+        const bool stop = last || (FILTER ? cand <= top_k + (top_k >> 3) + 8
+                                          : (cand <= kRankMax || (HC == 0 && fits)));
         __syncthreads();                                        // sel is rewritten next pass
         if (stop) break;
     }
@@ -331,8 +429,51 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
     if (tid == 0) n_gt = 0;
     __syncthreads();
     const bool gather_all = fits;
-    const int n_kept = gather_all ? n_above + n_tied : top_k;   // entries to sort
-    if (gather_all) {
+    int n_kept = gather_all ? n_above + n_tied : top_k;   // entries to sort
+    if constexpr (FILTER) {
+        // every entry of the row at or above the bound (the bound's bits below
+        // its digits are zero, so a key passes exactly when key >= kth): the
+        // held part, then the streamed rest, a chunk at a time, skipping the
+        // chunks whose largest key is below it
+        auto filter_chunk = [&](int64_t c, const u32x4 &kc) {
+            if (K::chunk_max(kc) >= kth) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const uint32_t full = K::at(kc, e);
+                    if (full >= kth) {
+                        const uint32_t at = atomicAdd(&n_gt, 1u);
+                        if (at < (uint32_t)kThreads) {
+                            ckey[at] = full;
+                            cidx[at] = (int32_t)(c * VEC + e);
+                        }
+                    }
+                }
+            }
+        };
+        for_chunks(filter_chunk);
+        auto filter_batch = [&](const u32x4 (&buf)[kUnroll], int64_t c0) {
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j) {
+                const int64_t c = c0 + (int64_t)j * kThreads;
+                if (c < nchunks) filter_chunk(c, K::from_raw(buf[j]));
+            }
+        };
+        // uniform trip count: every thread passes the same loads
+        constexpr int64_t kB = (int64_t)kUnroll * kThreads;   // chunks per batch
+        for (int64_t base = nheld; base < nchunks; base += 2 * kB) {
+            if (base + kB < nchunks) load_batch(sb, base + kB + tid);
+            filter_batch(sa, base + tid);
+            if (base + 2 * kB < nchunks) load_batch(sa, base + 2 * kB + tid);
+            filter_batch(sb, base + kB + tid);
+        }
+        __syncthreads();
+        const uint32_t total = n_gt;
+        if (total > (uint32_t)kThreads) {   // uniform: the buffer overflowed
+            __syncthreads();                // every thread has read n_gt
+            return false;
+        }
+        n_kept = (int)total;                // all of them are sorted; the first top_k are kept
+    } else if (gather_all) {
         opaque();
         for_chunks([&](int64_t c, const u32x4 &kc) {
 #pragma unroll
@@ -382,10 +523,10 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
         }
         eq_taken += chunk_total;
     };
-    if constexpr (CPT > 0) {
+    if constexpr (HC > 0) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            if ((int64_t)j * kThreads >= nchunks) break;   // uniform: every thread stops together
+        for (int j = 0; j < HC; ++j) {
+            if ((int64_t)j * kThreads >= nheld) break;   // uniform: every thread stops together
             compact((int64_t)j * kThreads, held[j]);
         }
     } else {
@@ -521,6 +662,23 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(
             store16(p + c * VEC, T::pack(o));
         });
     }
+    return true;
+}
+
+template <typename IO, int CPT>
+__global__ __launch_bounds__(kThreads) void topk_sample_kernel(
+    int32_t *token, IO *probs, const IO *logits, int64_t vocab, int64_t row_stride,
+    int64_t probs_stride, float inv_temp, int32_t top_k, const float *u) {
+    __shared__ SampleShared sh;
+    // the softmax output needs passes over the whole row anyway
+    if (CPT >= 0 || probs == nullptr) {
+        if (sample_row<IO, CPT>(sh, token, probs, logits, vocab, row_stride, probs_stride, inv_temp,
+                                top_k, u))
+            return;
+    }
+    if constexpr (CPT < 0)
+        sample_row<IO, 0>(sh, token, probs, logits, vocab, row_stride, probs_stride, inv_temp,
+                          top_k, u);
 }
 
 namespace {
@@ -545,7 +703,7 @@ void launch_typed(int32_t *token, void *probs, const void *logits, int64_t rows,
     else if (per_thread <= 2) NRS_TS(2);
     else if (per_thread <= 4) NRS_TS(4);
     else if (per_thread <= 8) NRS_TS(8);
-    else NRS_TS(0);
+    else NRS_TS(-8);
 #undef NRS_TS
 }
 

@@ -296,6 +296,28 @@ def test_sample_long_rows_ties(dt):
     assert tok.tolist() == [0, 8, 15]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_one_read_cases(dt):
+    # rows longer than the registers hold are read once: the held first part's k-th largest
+    # logit bounds the row's from below, and only logits at or above it are kept from the rest
+    V = 151936
+    ramp = torch.linspace(-8.0, 8.0, V)
+    # ascending: the whole rest of the row passes the bound (the buffer overflows, and the
+    # row is selected again over every logit); descending: none of it does
+    lg = W.store(torch.stack([ramp, ramp.flip(0), ramp, ramp.flip(0)]), dt)
+    tok, _ = sample_parity(lg, 1.0, 50, torch.tensor([0.0, 0.0, 0.6, 0.6], dtype=torch.float32),
+                           f"sample/long_ramp/{dt}", want_probs=False)
+    assert tok[1] == 0                                      # the largest logit comes first
+    # the largest logits all in the streamed part, below the buffer's size
+    lg = _logits(6, V, 3.0, dt, 47).float()
+    lg[:, V - 40:] = 20.0 + 0.01 * torch.arange(40, dtype=torch.float32)
+    sample_parity(W.store(lg, dt), 1.0, 50, _u(6, 48), f"sample/long_late_peaks/{dt}",
+                  want_probs=False)
+    # k = 300: more kept entries than the counting sort takes
+    lg = _logits(4, V, 3.0, dt, 49)
+    sample_parity(lg, 1.0, 300, _u(4, 50), f"sample/long_k300/{dt}", want_probs=False)
+
+
 def test_sample_long_rows_greedy_tied_maximum():
     lg = _logits(8, 151936, 4.0, "bf16", 45).float()
     top = lg.max(dim=1).values + 2.0
