@@ -97,6 +97,13 @@ template <> struct keys<float> {
     }
     __device__ static inline uint32_t max2(uint32_t a, uint32_t b) { return a > b ? a : b; }
     __device__ static inline uint32_t full(uint32_t m) { return m; }
+    // bit e set when element e's key is at least `bound` (a full key)
+    __device__ static inline uint32_t mask_ge(const u32x4 &k, uint32_t bound) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m |= (k[e] >= bound ? 1u : 0u) << e;
+        return m;
+    }
 };
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -131,6 +138,18 @@ template <> struct keys<__bf16> {
     __device__ static inline uint32_t full(uint32_t w) {
         const uint32_t lo = w & 0xFFFFu, hi = w >> 16, h = lo > hi ? lo : hi;
         return (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
+    }
+    // bit e set when element e's key is at least `bound`, a full key whose
+    // low 16 bits are zero (so comparing the 16-bit keys decides it)
+    __device__ static inline uint32_t mask_ge(const u32x4 &k, uint32_t bound) {
+        const uint32_t b16 = bound >> 16;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m |= ((k[i] & 0xFFFFu) >= b16 ? 1u : 0u) << (2 * i);
+            m |= ((k[i] >> 16) >= b16 ? 1u : 0u) << (2 * i + 1);
+        }
+        return m;
     }
 };
 
@@ -201,7 +220,8 @@ __device__ __attribute__((always_inline)) bool sample_row(
     constexpr bool FILTER = CPT < 0;
     constexpr int HC = FILTER ? -CPT : CPT;   // chunks held per thread
     constexpr int kDigitBits = HC > 0 ? 8 : 12;
-    constexpr int kRep = HC == 1 ? 8 : (HC > 0 ? 32 : 4);
+    // (the select over the threads' maxima counts one key per thread)
+    constexpr int kRep = FILTER ? 4 : (HC == 1 ? 8 : (HC > 0 ? 32 : 4));
     static_assert((kRep << kDigitBits) <= kHistWords, "histogram fits");
     uint32_t *hist = sh.hist, *wtot = sh.wtot, *sel = sh.sel, *ckey = sh.ckey;
     int *iscan = sh.iscan;
@@ -433,30 +453,58 @@ __device__ __attribute__((always_inline)) bool sample_row(
     if constexpr (FILTER) {
         // every entry of the row at or above the bound (the bound's bits below
         // its digits are zero, so a key passes exactly when key >= kth): the
-        // held part, then the streamed rest, a chunk at a time, skipping the
-        // chunks whose largest key is below it
-        auto filter_chunk = [&](int64_t c, const u32x4 &kc) {
-            if (K::chunk_max(kc) >= kth) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const uint32_t full = K::at(kc, e);
-                    if (full >= kth) {
-                        const uint32_t at = atomicAdd(&n_gt, 1u);
-                        if (at < (uint32_t)kThreads) {
-                            ckey[at] = full;
-                            cidx[at] = (int32_t)(c * VEC + e);
-                        }
+        // held part, then the streamed rest.  Each lane takes a bit mask of its
+        // passing entries per chunk, with no branch; a wave adds its lanes'
+        // counts with one scan and reserves their slots with one LDS atomic,
+        // and each lane then writes its entries in order.  (An atomic per
+        // passing entry, behind a branch per entry, took about 4x as long.)
+        const int lane = tid & 63;
+        auto append = [&](const uint32_t *masks, const u32x4 *kcs, const int64_t *cs, int n) {
+            int cnt = 0;
+            for (int j = 0; j < n; ++j) cnt += __builtin_popcount(masks[j]);
+            const int incl = wave_incl_scan(cnt);
+            const int wave_total = __shfl(incl, 63, 64);
+            if (wave_total == 0) return;                 // uniform over the wave
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&n_gt, (uint32_t)wave_total);
+            base = (uint32_t)__shfl((int)base, 0, 64);
+            uint32_t pos = base + (uint32_t)(incl - cnt);
+            for (int j = 0; j < n; ++j) {
+                uint32_t m = masks[j];
+                while (m) {
+                    const int e = __builtin_ctz(m);
+                    m &= m - 1;
+                    if (pos < (uint32_t)kThreads) {
+                        ckey[pos] = K::at(kcs[j], e);
+                        cidx[pos] = (int32_t)(cs[j] * VEC + e);
                     }
+                    ++pos;
                 }
             }
         };
-        for_chunks(filter_chunk);
+        {
+            uint32_t masks[HC];
+            u32x4 kcs[HC];
+            int64_t cs[HC];
+#pragma unroll
+            for (int j = 0; j < HC; ++j) {
+                cs[j] = tid + (int64_t)j * kThreads;
+                kcs[j] = held[j];
+                masks[j] = K::chunk_max(held[j]) >= kth ? K::mask_ge(held[j], kth) : 0u;
+            }
+            append(masks, kcs, cs, HC);
+        }
         auto filter_batch = [&](const u32x4 (&buf)[kUnroll], int64_t c0) {
+            uint32_t masks[kUnroll];
+            u32x4 kcs[kUnroll];
+            int64_t cs[kUnroll];
 #pragma unroll
             for (int j = 0; j < kUnroll; ++j) {
-                const int64_t c = c0 + (int64_t)j * kThreads;
-                if (c < nchunks) filter_chunk(c, K::from_raw(buf[j]));
+                cs[j] = c0 + (int64_t)j * kThreads;
+                kcs[j] = K::from_raw(buf[j]);
+                masks[j] = (cs[j] < nchunks && K::chunk_max(kcs[j]) >= kth) ? K::mask_ge(kcs[j], kth) : 0u;
             }
+            append(masks, kcs, cs, kUnroll);
         };
         // uniform trip count: every thread passes the same loads
         constexpr int64_t kB = (int64_t)kUnroll * kThreads;   // chunks per batch
@@ -464,7 +512,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
             if (base + kB < nchunks) load_batch(sb, base + kB + tid);
             filter_batch(sa, base + tid);
             if (base + 2 * kB < nchunks) load_batch(sa, base + 2 * kB + tid);
-            filter_batch(sb, base + kB + tid);
+            if (base + kB < nchunks) filter_batch(sb, base + kB + tid);
         }
         __syncthreads();
         const uint32_t total = n_gt;
