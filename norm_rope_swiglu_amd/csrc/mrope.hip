@@ -523,8 +523,14 @@ hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t 
     }
     // as for M-RoPE, small calls take one token per block (measured at the
     // 5-token decode step: 2.77 -> 2.55 us per call), and tokens of at most 64
-    // items aim at ~256 threads (H = 512 bf16 at 32768 tokens: 7% faster)
-    int tpb = nt ? (per_tok <= 64 ? 256 : 512) / per_tok : 1;
+    // items aim at ~256 threads (H = 512 bf16 at 32768 tokens: 7% faster).
+    // Tokens of 65-256 items aim at 1024 threads, so each kv head's cache rows
+    // are written 4 slots (1 KiB) at a time instead of 2: measured at 32768
+    // tokens, bf16 head_dim 128, H = 2048 89.3 -> 86.8 us, H = 1024 the same
+    // (47.3 -> 47.1 us); H = 4096 (512 items a token) 2% slower with 2 tokens
+    // a block, and 8 tokens a block (a second pass over the items) slower at
+    // every width.
+    int tpb = nt ? (per_tok <= 64 ? 256 : (per_tok <= 256 ? 1024 : 512)) / per_tok : 1;
     if (tpb < 1) tpb = 1;
     int threads = ((tpb * per_tok + 63) / 64) * 64;
     if (threads > kMaxThreads) threads = kMaxThreads;

@@ -146,6 +146,19 @@ def test_kv_append_small_tokens_streaming():
               max_seq=(T + 1) // 2, tag="kv/small_tokens_stream", rows=rows)
 
 
+@pytest.mark.parametrize("hidden,T", [(1024, 8195), (2048, 8197)])
+def test_kv_append_1024_thread_blocks_streaming(hidden, T):
+    # tokens of 128 and 256 items at a streaming size: 8 and 4 tokens per 1024-thread block,
+    # a part-filled last block, slots shuffled over two sequences
+    w = W.sweep(dtype="bf16", hidden=hidden, head_dim=128, tokens=T, device="cuda")
+    g = torch.Generator().manual_seed(8)
+    perm = torch.randperm(T, generator=g)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, 2, 3, 4, T - 5, T - 3, T - 2, T - 1]),
+                                   torch.randint(0, T, (55,), generator=g)]))
+    kv_parity(w, seq_idx=(perm % 2).tolist(), slot=(perm // 2).tolist(), n_seqs=2,
+              max_seq=(T + 1) // 2, tag=f"kv/blocks1024/H{hidden}", rows=rows)
+
+
 def test_kv_append_full_size_sampled():
     w = W.sweep(dtype="bf16", hidden=2048, head_dim=128, tokens=32768, device="cuda")
     g = torch.Generator().manual_seed(3)
