@@ -482,8 +482,9 @@ hipError_t launch_mrope_kv(void *q, const void *k, const void *v, const int32_t 
     const bool nt = tokens * (long long)(2 * n_q + 4 * n_kv) * head_dim * (dtype == 0 ? 4 : 2) >=
                     kStreamBytes;
     if (cph == 1 || cph == 2 || cph == 4) {
-        // half-heads under a cache line: mrope_kv_narrow_kernel, chunks per
-        // thread and token blocking as for M-RoPE's narrow kernel
+        // half-heads under a cache line: mrope_kv_narrow_kernel, two chunks
+        // per thread (a block's width apart) in streaming calls, one in small
+        // ones, and about 512 threads' worth of whole tokens per block
         const int cpt = 2 * per_tok;
         const int u = nt ? narrow_per_thread<true>() : narrow_per_thread<false>();
         int tpb = nt ? 512 * u / cpt : 1;
