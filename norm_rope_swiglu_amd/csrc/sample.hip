@@ -313,9 +313,9 @@ __device__ __attribute__((always_inline)) bool sample_row(
     //    the top (streamed bf16 keys: 12 + 4 bits; fp32: 12 + 12 + 8).  The
     //    remaining digits are left to the sort once every key above the
     //    selected bin plus the bin itself fits the counting sort (256), or, for a
-    //    streamed row, the 1024-entry gather buffer (with 12-bit digits this
-    //    usually happens after the first pass, so a streamed row is read twice:
-    //    once counted, once gathered).  The
+    //    streamed row (CPT == 0: a long row that fell back), the 1024-entry
+    //    gather buffer (with 12-bit digits this usually happens after the first
+    //    pass, so such a row is read twice: once counted, once gathered).  The
     //    histograms keep replicas (indexed by lane) so lanes counting the same
     //    bin, common with peaky logits, split over several addresses.
     constexpr int kKeyBits = sizeof(IO) == 4 ? 32 : 16;   // bits that vary in a key
