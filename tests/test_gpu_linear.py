@@ -168,6 +168,16 @@ def test_gemm_big_tiles_short_inputs(n_in):
     lin_parity(x, w, 1e-6, f"lin/gemm/big_short{n_in}", rows=rows)
 
 
+def test_gemm_benchmark_shape_sampled_rows():
+    # the benchmark's large GEMM launch: 32768 x 2048 -> 4096 (256 x 256 tiles, 64 stages),
+    # 64 rows against the oracle, the first and last of the first and last tiles among them
+    x, w = lin_inputs(32768, 2048, 4096, "bf16", 18)
+    g = torch.Generator().manual_seed(19)
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, 255, 256, 32511, 32512, 32766, 32767]),
+                                   torch.randint(0, 32768, (56,), generator=g)]))
+    lin_parity(x, w, 1e-6, "lin/gemm/bench32768", rows=rows)
+
+
 def test_gemm_strided_operands():
     xb, wb = lin_inputs(200, 640, 96, "bf16", 11)
     lin_parity(xb[:, 64:576], wb[:, 128:640], 1e-6, "lin/gemm/strided")

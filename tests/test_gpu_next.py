@@ -331,6 +331,13 @@ def test_sample_long_rows_one_read_cases(dt):
     sample_parity(lg, 1.0, 300, _u(4, 50), f"sample/long_k300/{dt}", want_probs=False)
 
 
+def test_sample_benchmark_batch_every_row():
+    # the benchmark's sampler launch: 256 rows x 151936 bf16 logits, k 50, token only; every
+    # row against the oracle's full sort
+    lg = _logits(256, 151936, 3.0, "bf16", 51)
+    sample_parity(lg, 1.0, 50, _u(256, 52), "sample/bench256x151936", want_probs=False)
+
+
 def test_sample_long_rows_greedy_tied_maximum():
     lg = _logits(8, 151936, 4.0, "bf16", 45).float()
     top = lg.max(dim=1).values + 2.0
