@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
 // into slabs.
 template <typename IO, bool NT, int CPH>
 __global__ __launch_bounds__(64) void mrope_wave_kernel(
-    mrope_freqs fr, IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int32_t tokens,
+    [[maybe_unused]] mrope_freqs fr, IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int32_t tokens,
     int32_t half, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
     int32_t q_cpt, int32_t k_cpt, int32_t q_waves, fastdiv div_q_cpt, fastdiv div_k_cpt,
     fastdiv div_half) {

@@ -82,7 +82,6 @@ __device__ inline float value_of(uint32_t k) {
 template <typename IO> struct keys;
 
 template <> struct keys<float> {
-    static constexpr int VEC = 4;
     __device__ static inline u32x4 from_raw(const u32x4 &raw) {
         u32x4 k;
 #pragma unroll
@@ -109,7 +108,6 @@ template <> struct keys<float> {
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 template <> struct keys<__bf16> {
-    static constexpr int VEC = 8;
     __device__ static inline uint32_t key16(uint32_t h) {
         if (h == 0x8000u) h = 0u;                       // -0 onto +0
         return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
