@@ -33,10 +33,12 @@
 // pass runs over the registers.  (At 20 chunks per thread the registers spill
 // and the kernel ran slower than streaming the row.)  Longer rows, when only
 // the token is asked for, are read once too: the first 8 chunks per thread
-// are held, the top_k-th largest of the threads' maxima (a lower bound for
-// the row's top_k-th largest) is selected, and one pass over the held keys and
-// the streamed rest keeps every logit at or above it (about 2.5 top_k of
-// them), which step 3 sorts.  Such a row falls back to the passes above,
+// are held as loaded, each thread's largest logit is found with packed
+// compares, a lower bound for the row's top_k-th largest is taken from those
+// maxima (the waves sort theirs across the lanes; the bound is the top_k-th
+// largest of every wave's first 8 or 16), and one pass over the held part and
+// the streamed rest tests the loaded values against it and keeps, as keys,
+// every logit at or above it (about 2.5 top_k of them), which step 3 sorts.  Such a row falls back to the passes above,
 // re-reading it, only when the kept logits overflow the 1024-entry buffer
 // (top_k near 1024, or a row whose logits rise along it), or when the softmax
 // output is asked for.
@@ -62,6 +64,9 @@ constexpr int kHistWords = 16384;
 // up to this many kept entries are ranked by counting; more by a bitonic
 // network (counting grows as entries squared over the 1024 threads)
 constexpr int kRankMax = 256;
+// rows filtered against a bound take it from the waves' leading thread
+// maxima up to this top_k (a radix select over all the maxima beyond)
+constexpr int kLeadTopK = 128;
 
 // Order-preserving map of an fp32 value to uint32 (larger value, larger key);
 // -0 is folded onto +0 so equal values have equal keys.
@@ -180,6 +185,189 @@ __device__ inline float block_inclusive_scan(float v, float *wave_tot) {
     __syncthreads();
     return before + incl;
 }
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// v from lane ^ J (J a power of two below 64): DPP moves within a 16-lane
+// row (quad permutes for 1 and 2, the row shifted up or down by 4, the row
+// rotated by 8), ds_swizzle within 32 lanes for 16, a lane permute for 32.
+template <int J> __device__ inline uint32_t lane_xor(uint32_t v) {
+    const int iv = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4) {
+        const int up = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0xF, false);   // row_shl:4: lane + 4
+        const int dn = __builtin_amdgcn_update_dpp(iv, iv, 0x114, 0xF, 0xF, false);   // row_shr:4: lane - 4
+        return (uint32_t)((threadIdx.x & 4) ? dn : up);
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (J == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(iv, (16 << 10) | 0x1F);           // xor 16 in 32
+    } else {
+        return (uint32_t)__shfl_xor(iv, J, 64);
+    }
+}
+
+// A bitonic network across the lanes: compare-exchange of lanes (lane,
+// lane ^ J); in a block of SIZE lanes to be sorted descending the lower lane
+// keeps the larger key.
+template <int SIZE, int J> __device__ inline uint32_t bitonic_step(uint32_t v, int lane) {
+    const uint32_t o = lane_xor<J>(v);
+    const bool keep_max = ((lane & J) == 0) == ((lane & SIZE) == 0);
+    return keep_max ? (v > o ? v : o) : (v < o ? v : o);
+}
+template <int SIZE, int J> __device__ inline uint32_t bitonic_merge(uint32_t v, int lane) {
+    v = bitonic_step<SIZE, J>(v, lane);
+    if constexpr (J > 1) return bitonic_merge<SIZE, J / 2>(v, lane);
+    else return v;
+}
+template <int SIZE> __device__ inline uint32_t bitonic_sort(uint32_t v, int lane) {
+    if constexpr (SIZE > 2) v = bitonic_sort<SIZE / 2>(v, lane);
+    return bitonic_merge<SIZE, SIZE / 2>(v, lane);
+}
+
+// The wave's 64 keys sorted across the lanes, descending (lane 0 the largest).
+__device__ inline uint32_t wave_sort_desc(uint32_t v) {
+    return bitonic_sort<64>(v, threadIdx.x & 63);
+}
+
+// A workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight (__syncthreads also waits for every one of them).
+__device__ inline void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// max(v, v of lane ^ J).  The partner's value is read before the compare:
+// a cross-lane read inside a branch (as a conditional operator evaluates its
+// arms) would read lanes the branch has switched off.
+template <int J> __device__ inline uint32_t max_xor(uint32_t v) {
+    const uint32_t o = lane_xor<J>(v);
+    return v > o ? v : o;
+}
+
+// The largest of the wave's 64 keys, in every lane.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    v = max_xor<1>(v);
+    v = max_xor<2>(v);
+    v = max_xor<4>(v);
+    v = max_xor<8>(v);
+    const int b = (int)v;
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(b, 0), r1 = (uint32_t)__builtin_amdgcn_readlane(b, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane(b, 32), r3 = (uint32_t)__builtin_amdgcn_readlane(b, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, c = r2 > r3 ? r2 : r3;
+    return a > c ? a : c;
+}
+
+// The full order key of one bf16 pattern h (as keys<__bf16>::at gives it).
+__device__ inline uint32_t bf16_full_key(uint32_t h) {
+    const uint32_t k = keys<__bf16>::key16(h);
+    return (k << 16) | ((k & 0x8000u) ? 0u : 0xFFFFu);
+}
+
+// The order key of entry e of a chunk as loaded.
+template <typename IO> __device__ inline uint32_t raw_key(const u32x4 &raw, int e) {
+    if constexpr (sizeof(IO) == 2) return bf16_full_key((raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    else return key_of(__builtin_bit_cast(float, (unsigned)raw[e]));
+}
+
+// The largest logit of N chunks as loaded, as an order key, with no per-entry
+// key: bf16 patterns compare as signed 16-bit integers in value order while a
+// non-negative one exists, and among negative ones the least unsigned pattern
+// is the largest value (packed max and min, two patterns an op); fp32 takes
+// the float max.
+template <typename IO, int N> __device__ inline uint32_t max_key_raw(const u32x4 (&c)[N]) {
+    if constexpr (sizeof(IO) == 2) {
+        s16x2 mx = {(short)-32768, (short)-32768};
+        us2 mn = {(unsigned short)0xFFFF, (unsigned short)0xFFFF};
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(s16x2, (unsigned)c[j][i]));
+                mn = __builtin_elementwise_min(mn, __builtin_bit_cast(us2, (unsigned)c[j][i]));
+            }
+        const int hmax = mx.x > mx.y ? mx.x : mx.y;
+        return bf16_full_key(hmax >= 0 ? (uint32_t)hmax : (uint32_t)(mn.x < mn.y ? mn.x : mn.y));
+    } else {
+        float m = -__builtin_huge_valf();
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, __builtin_bit_cast(float, (unsigned)c[j][i]));
+        return key_of(m);
+    }
+}
+
+// A bound on order keys tested on chunks as loaded.  A bound above zero and
+// finite (the usual case) is compared with the loaded values: bf16 patterns
+// as signed 16-bit integers (negative patterns fall below it) by a saturating
+// packed subtract, whose sign bit is set where an entry falls below; fp32 as
+// floats.  Any other bound is compared on order keys.
+template <typename IO> struct RawBound {
+    uint32_t key, hb;
+    float bval;
+    bool fast;
+    // k is the same in every lane: held in a scalar register, so the choice
+    // between the two tests is a uniform branch (as a per-lane value the
+    // compiler evaluated both tests for every chunk)
+    __device__ explicit RawBound(uint32_t k)
+        : key((uint32_t)__builtin_amdgcn_readfirstlane((int)k)), hb(0u), bval(0.0f) {
+        k = key;
+        if constexpr (sizeof(IO) == 2) {
+            hb = (k >> 16) & 0x7FFFu;   // a bf16 key's low 16 bits follow its sign
+            fast = (k & 0x80000000u) && hb != 0u;
+        } else {
+            const uint32_t mag = k & 0x7FFFFFFFu;
+            fast = (k & 0x80000000u) && mag - 1u < 0x7F800000u;
+            bval = __builtin_bit_cast(float, mag);
+        }
+    }
+    // whether any entry of the chunk is at or above the bound
+    __device__ bool any(const u32x4 &raw) const {
+        if (fast) {
+            if constexpr (sizeof(IO) == 2) {
+                const s16x2 b2 = {(short)hb, (short)hb};
+                uint32_t all = 0xFFFFFFFFu;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    all &= __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
+                                                             __builtin_bit_cast(s16x2, (unsigned)raw[i]), b2));
+                return (all & 0x80008000u) != 0x80008000u;
+            } else {
+                bool p = false;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p |= __builtin_bit_cast(float, (unsigned)raw[i]) >= bval;
+                return p;
+            }
+        }
+        return keys<IO>::chunk_max(keys<IO>::from_raw(raw)) >= key;
+    }
+    // bit e set when entry e is at or above the bound
+    __device__ uint32_t mask(const u32x4 &raw) const {
+        if (fast) {
+            uint32_t m = 0u;
+            if constexpr (sizeof(IO) == 2) {
+                const s16x2 b2 = {(short)hb, (short)hb};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t d = ~__builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
+                                                                         __builtin_bit_cast(s16x2, (unsigned)raw[i]), b2));
+                    m |= ((d >> 15) & 1u) << (2 * i);
+                    m |= (d >> 31) << (2 * i + 1);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m |= (__builtin_bit_cast(float, (unsigned)raw[i]) >= bval ? 1u : 0u) << i;
+            }
+            return m;
+        }
+        return keys<IO>::mask_ge(keys<IO>::from_raw(raw), key);
+    }
+};
 }  // namespace
 
 // The workgroup's LDS, shared by a row's first attempt and its fallback.
@@ -194,7 +382,8 @@ struct SampleShared {
     alignas(16) int32_t cidx[kThreads];
     float csum[kThreads];       // prefix sums of the kept weights
     int32_t rank_of[kThreads];  // ranks of the kept entries (up to kRankMax)
-    uint32_t n_gt;
+    alignas(16) uint32_t lead[kThreads / 4];   // the waves' largest thread maxima
+    uint32_t n_gt, lead_bound;
     int32_t pick;
 };
 
@@ -244,14 +433,16 @@ __device__ __attribute__((always_inline)) bool sample_row(
     // is issued with the held part.  These loads take no branch (an index past
     // the row reads its last chunk, skipped by the filter), so the compiler
     // waits for each batch alone rather than for every load in flight.
-    // Measured on MI355X (256 x 151936 bf16): issuing a second batch with the
-    // held part, or the first three batches as straight-line code, made the
-    // call 7% slower (the held part, which the select waits for, then lands
-    // later).
-    u32x4 sa[FILTER ? kUnroll : 1], sb[FILTER ? kUnroll : 1];
-    auto load_batch = [&](u32x4 (&buf)[FILTER ? kUnroll : 1], int64_t c0) {
+    // Measured on MI355X (256 x 151936 bf16, 23.6 us as written): issuing the
+    // second batch with the held part too made the call 24.7 us, every batch
+    // at once (six chunks per thread) 25.7 us, and issuing the first two only
+    // once a wave's held part had landed 25.1 us: the held part, which the
+    // bound waits for, lands later.
+    constexpr int FB = FILTER ? kUnroll : 1;
+    u32x4 sa[FB], sb[FB];
+    auto load_batch = [&](u32x4 (&buf)[FB], int64_t c0) {
 #pragma unroll
-        for (int j = 0; j < (FILTER ? kUnroll : 1); ++j) {
+        for (int j = 0; j < FB; ++j) {
             const int64_t c = c0 + (int64_t)j * kThreads;
             buf[j] = load16(x + (c < nchunks ? c : nchunks - 1) * VEC);
         }
@@ -267,7 +458,9 @@ __device__ __attribute__((always_inline)) bool sample_row(
             if (c < nheld) held[j] = load16(x + c * VEC);
         }
     }
-    if constexpr (HC > 0) {
+    // (a row filtered against a bound keeps its chunks as loaded: keys are
+    // formed only for the entries it keeps)
+    if constexpr (HC > 0 && !FILTER) {
 #pragma unroll
         for (int j = 0; j < HC; ++j) held[j] = K::from_raw(held[j]);
     }
@@ -322,21 +515,55 @@ __device__ __attribute__((always_inline)) bool sample_row(
     // is at most the row's top_k-th largest: every kept entry lies at or
     // above it.  With top_k well below the thread count, the row's largest
     // entries mostly sit in different threads, and the bound is nearly the
-    // row's own top_k-th largest.
+    // row's own top_k-th largest.  (Up to top_k = kLeadTopK the bound comes
+    // from the waves' sorted maxima instead, below.)
     uint32_t mkey = 0;
     if constexpr (FILTER) {
-        uint32_t w = 0;
-        for_chunks([&](int64_t, const u32x4 &kc) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w = K::max2(w, kc[i]);
-        });
-        mkey = K::full(w);
+        mkey = max_key_raw<IO, HC>(held);   // every held chunk is in the row
     }
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)top_k;
     const uint32_t rep = tid & (kRep - 1);
     bool fits = false;
     constexpr int kPasses = (kKeyBits + kDigitBits - 1) / kDigitBits;
+    // FILTER, top_k <= kLeadTopK: the bound is instead the top_k-th largest
+    // of the waves' m largest thread maxima (m = 8, or 16 past top_k = 64),
+    // the waves sorting their maxima across the lanes; ranked by counting
+    // over those 16 * m keys.  They are distinct entries of the row too, and
+    // with the row's largest entries spread over the threads, the waves'
+    // first eight or sixteen hold nearly all that matter: on rows of 151,936
+    // normally distributed logits, top_k = 50, it keeps 118.6 entries on
+    // average against 118.1 for the exact top_k-th of all 1024 maxima.  One
+    // sort in registers and two barriers that leave the streamed batch in
+    // flight, in place of a radix select's passes (which waited for it).
+    const bool lead = FILTER && top_k <= kLeadTopK;   // uniform
+    if (lead) {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int m = top_k <= 64 ? 8 : 16;
+        const uint32_t srt = wave_sort_desc(mkey);
+        if (lane < m) sh.lead[wave * m + lane] = srt;
+        if (tid == 0) sh.lead_bound = 0u;
+        lds_sync();   // the streamed batches stay in flight
+        const int na = kWaves * m;
+        uint32_t cand = 0u;
+        if (tid < na) {
+            const uint32_t a = sh.lead[tid];
+            int ge = 0;
+            for (int j = 0; j < na; j += 4) {
+                const u32x4 q = *reinterpret_cast<const u32x4 *>(&sh.lead[j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ge += q[e] >= a ? 1 : 0;
+            }
+            cand = ge >= top_k ? a : 0u;   // the bound: the largest such key
+        }
+        if (wave * 64 < na) {
+            cand = wave_max_u32(cand);
+            if (lane == 0) atomicMax(&sh.lead_bound, cand);
+        }
+        lds_sync();
+        prefix = sh.lead_bound;
+    }
+    if (!lead) {
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
         // digit bits [shift, top): constants once the loop is unrolled
@@ -432,6 +659,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
         __syncthreads();                                        // sel is rewritten next pass
         if (stop) break;
     }
+    }   // !lead
     // keys below the selected digits are either left to the sort (fits) or
     // fixed (bf16: the low 16 bits follow the sign), so one representative
     // key decides the comparisons
@@ -449,15 +677,19 @@ __device__ __attribute__((always_inline)) bool sample_row(
     const bool gather_all = fits;
     int n_kept = gather_all ? n_above + n_tied : top_k;   // entries to sort
     if constexpr (FILTER) {
-        // every entry of the row at or above the bound (the bound's bits below
-        // its digits are zero, so a key passes exactly when key >= kth): the
-        // held part, then the streamed rest.  Each lane takes a bit mask of its
-        // passing entries per chunk, with no branch; a wave adds its lanes'
-        // counts with one scan and reserves their slots with one LDS atomic,
-        // and each lane then writes its entries in order.  (An atomic per
-        // passing entry, behind a branch per entry, took about 4x as long.)
+        // every entry of the row at or above the bound (a key passes exactly
+        // when key >= kth: the bound's bits below its digits are zero, or, from
+        // the waves' leading maxima, it is a key itself): the held part, then
+        // the streamed rest, both tested as loaded (RawBound), and a chunk's
+        // bit mask of its passing entries formed only when one passes.  A wave
+        // adds its lanes' counts with one scan and reserves their slots with
+        // one LDS atomic, and each lane then writes its entries, as keys, in
+        // order.  (An atomic per passing entry, behind a branch per entry, took
+        // about 4x as long; forming every entry's key before the test spent
+        // about 12 vector operations per logit.)
         const int lane = tid & 63;
-        auto append = [&](const uint32_t *masks, const u32x4 *kcs, const int64_t *cs, int n) {
+        const RawBound<IO> bnd(kth);
+        auto append = [&](const uint32_t *masks, const u32x4 *raws, const int64_t *cs, int n) {
             int cnt = 0;
             for (int j = 0; j < n; ++j) cnt += __builtin_popcount(masks[j]);
             const int incl = wave_incl_scan(cnt);
@@ -473,7 +705,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
                     const int e = __builtin_ctz(m);
                     m &= m - 1;
                     if (pos < (uint32_t)kThreads) {
-                        ckey[pos] = K::at(kcs[j], e);
+                        ckey[pos] = raw_key<IO>(raws[j], e);
                         cidx[pos] = (int32_t)(cs[j] * VEC + e);
                     }
                     ++pos;
@@ -482,30 +714,27 @@ __device__ __attribute__((always_inline)) bool sample_row(
         };
         {
             uint32_t masks[HC];
-            u32x4 kcs[HC];
             int64_t cs[HC];
 #pragma unroll
             for (int j = 0; j < HC; ++j) {
                 cs[j] = tid + (int64_t)j * kThreads;
-                kcs[j] = held[j];
-                masks[j] = K::chunk_max(held[j]) >= kth ? K::mask_ge(held[j], kth) : 0u;
+                masks[j] = bnd.any(held[j]) ? bnd.mask(held[j]) : 0u;
             }
-            append(masks, kcs, cs, HC);
+            append(masks, held, cs, HC);
         }
-        auto filter_batch = [&](const u32x4 (&buf)[kUnroll], int64_t c0) {
-            uint32_t masks[kUnroll];
-            u32x4 kcs[kUnroll];
-            int64_t cs[kUnroll];
+        auto filter_batch = [&](const u32x4 (&buf)[FB], int64_t c0) {
+            uint32_t masks[FB];
+            int64_t cs[FB];
 #pragma unroll
-            for (int j = 0; j < kUnroll; ++j) {
+            for (int j = 0; j < FB; ++j) {
                 cs[j] = c0 + (int64_t)j * kThreads;
-                kcs[j] = K::from_raw(buf[j]);
-                masks[j] = (cs[j] < nchunks && K::chunk_max(kcs[j]) >= kth) ? K::mask_ge(kcs[j], kth) : 0u;
+                masks[j] = (cs[j] < nchunks && bnd.any(buf[j])) ? bnd.mask(buf[j]) : 0u;
             }
-            append(masks, kcs, cs, kUnroll);
+            append(masks, buf, cs, FB);
         };
         // uniform trip count: every thread passes the same loads
-        constexpr int64_t kB = (int64_t)kUnroll * kThreads;   // chunks per batch
+        constexpr int64_t kB = (int64_t)FB * kThreads;   // chunks per batch
+        // (the first two batches were issued with the held part)
         for (int64_t base = nheld; base < nchunks; base += 2 * kB) {
             if (base + kB < nchunks) load_batch(sb, base + kB + tid);
             filter_batch(sa, base + tid);
@@ -685,8 +914,9 @@ __device__ __attribute__((always_inline)) bool sample_row(
         if (tid == 0) token[row] = pick >= 0 ? pick : cidx[top_k - 1];
     }
 
-    // optional full softmax row
-    if (probs) {
+    // optional full softmax row (never asked of a row filtered against a
+    // bound, which keeps its chunks as loaded)
+    if (!FILTER && probs) {
         opaque();
         float part = 0.0f;
         for_chunks([&](int64_t, const u32x4 &kc) {

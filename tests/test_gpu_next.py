@@ -347,6 +347,97 @@ def test_sample_long_rows_greedy_tied_maximum():
     assert torch.all(tok == 120000)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_equal_maxima_in_few_threads(dt):
+    # 200 equal maxima packed into the chunks of a few threads (thread t holds chunks t,
+    # t + 1024, ...; 8 or 4 logits a chunk), k = 30: the bound, taken from each thread's
+    # largest logit, counts each such thread once, and the kept set is the 30 lowest-index
+    # maxima
+    V = 151936
+    vec = 8 if dt == "bf16" else 4
+    lg = _logits(4, V, 1.0, dt, 61).float()
+    nch = V // vec
+    idx = sorted((t + 1024 * j) * vec + e for t in (3, 700) for j in range(nch // 1024 + 1)
+                 for e in range(vec) if t + 1024 * j < nch)[:200]
+    assert len(idx) == 200
+    lg[:, idx] = 5.0
+    lg = W.store(lg, dt)
+    u = torch.tensor([0.0, 0.25, 0.5, 0.999], dtype=torch.float32)
+    tok, _ = sample_parity(lg, 1.0, 30, u, f"sample/long_packed_maxima/{dt}", want_probs=False)
+    assert tok[0] == min(idx)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_many_equal_maxima(dt):
+    # 400 equal maxima spread over the row, k = 50: all of them pass the bound, and the
+    # sort keeps the 50 lowest-index maxima
+    V = 151936
+    g = torch.Generator().manual_seed(62)
+    lg = _logits(3, V, 1.0, dt, 63).float()
+    for r in range(3):
+        lg[r, torch.randperm(V, generator=g)[:400]] = 6.0
+    lg = W.store(lg, dt)
+    u = torch.tensor([0.0, 0.5, 0.9999], dtype=torch.float32)
+    tok, _ = sample_parity(lg, 1.0, 50, u, f"sample/long_equal_maxima/{dt}", want_probs=False)
+    first = [int(torch.nonzero(lg[r].float() == 6.0)[0]) for r in range(3)]
+    assert tok[0] == first[0]
+
+
+@pytest.mark.parametrize("dt,vocab,k,rows", [("bf16", 65544, 128, 5), ("bf16", 151936, 1, 6),
+                                             ("bf16", 65544, 50, 600), ("f32", 151936, 50, 3),
+                                             ("bf16", 262144, 20, 3)])
+def test_sample_long_rows_shapes(dt, vocab, k, rows):
+    # k = 128 (the bound from each wave's 16 leading maxima), greedy, 600 rows, fp32, and
+    # a 262,144-logit row (several streamed batches past the held part)
+    lg = _logits(rows, vocab, 3.0, dt, 64)
+    sample_parity(lg, 0.8, k, _u(rows, 65), f"sample/long/{dt}/V{vocab}/k{k}/R{rows}",
+                  want_probs=False)
+
+
+def test_sample_long_rows_back_to_back_calls():
+    # long-row calls of different shapes and k in a row on one stream, then again, every
+    # one checked
+    cases = [("bf16", 151936, 50, 8), ("bf16", 65544, 64, 20), ("f32", 151936, 40, 4),
+             ("bf16", 151936, 3, 8)]
+    for rep in range(2):
+        for i, (dt, V, k, R) in enumerate(cases):
+            lg = _logits(R, V, 3.0, dt, 70 + i)
+            sample_parity(lg, 1.0, k, _u(R, 80 + i + rep), f"sample/b2b/{rep}/{i}",
+                          want_probs=False)
+
+
+def test_sample_long_rows_graph_replays():
+    # long-row calls captured in a graph and replayed several times with eager calls
+    # between: every replay gives the eager tokens
+    R, V = 64, 151936
+    lgs = [_logits(R, V, 3.0, "bf16", 90 + i).cuda() for i in range(3)]
+    us = [_u(R, 95 + i).cuda() for i in range(3)]
+    toks = [torch.empty(R, dtype=torch.int32, device="cuda") for _ in range(3)]
+    want = [nrs.softmax_topk_sample(lgs[i], 1.0, 50, us[i]).cpu() for i in range(3)]
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        nrs.softmax_topk_sample(lgs[0], 1.0, 50, us[0], token=toks[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for i in range(3):
+            nrs.softmax_topk_sample(lgs[i], 1.0, 50, us[i], token=toks[i])
+    for rep in range(4):
+        for t in toks:
+            t.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(toks[i].cpu(), want[i]), f"replay {rep} call {i}"
+        other = nrs.softmax_topk_sample(lgs[(rep + 1) % 3], 1.0, 50, us[(rep + 1) % 3]).cpu()
+        assert torch.equal(other, want[(rep + 1) % 3]), f"eager call after replay {rep}"
+    # and against the oracle once
+    otok, _, kept, _ = oracle.softmax_topk_sample(lgs[0].cpu(), 1.0, 50, us[0].cpu().numpy(),
+                                                  want_probs=False)
+    for r in range(R):
+        assert int(want[0][r]) in kept[r].tolist()
+
+
 def test_sample_greedy_is_first_argmax():
     lg = _logits(64, 3072, 4.0, "f32", 5)
     lg[:, 1234] = lg.max(dim=1).values + 1.0
