@@ -438,6 +438,40 @@ def test_sample_long_rows_graph_replays():
         assert int(want[0][r]) in kept[r].tolist()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_bound_at_or_below_zero(dt):
+    # the long-row filter tests loaded values against a bound above zero and compares order
+    # keys otherwise: rows of negative logits (log-probabilities), and rows whose k-th value
+    # is exactly zero with +0 and -0 both present (equal logits, kept by index)
+    V = 151936
+    neg = -(_logits(3, V, 2.0, dt, 71).float().abs() + 0.5)
+    sample_parity(W.store(neg, dt), 1.0, 50, _u(3, 72), f"sample/long_negative/{dt}",
+                  want_probs=False)
+    z = torch.zeros(3, V)
+    z[:, 1::2] = -0.0                                  # signed zeros interleaved
+    z[:, [100, 5000, 90000, 150000]] = torch.tensor([3.0, 2.0, 1.0, 0.5])
+    z[:, 7] = -1.0
+    tok, _ = sample_parity(W.store(z, dt), 1.0, 20, torch.tensor([0.0, 0.99, 0.9999], dtype=torch.float32),
+                           f"sample/long_zero_bound/{dt}", want_probs=False)
+    assert tok[0] == 100
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sample_long_rows_non_finite_logits_give_a_valid_index(dt):
+    # NaN logits, and infinite ones (exp(inf - inf) is NaN here as in fp64), give an
+    # unspecified token, but always one of the row's indices
+    V = 151936
+    lg = _logits(6, V, 3.0, dt, 74).float()
+    lg[0, ::3] = float("nan")
+    lg[1, :] = float("nan")
+    lg[2, 12345] = float("nan")
+    lg[3, [40000, 20]] = float("inf")
+    lg[4, :] = -float("inf")
+    lg[5, ::2] = float("inf")
+    tok = nrs.softmax_topk_sample(W.store(lg, dt).cuda(), 1.0, 50, _u(6, 75).cuda()).cpu()
+    assert torch.all((tok >= 0) & (tok < V))
+
+
 def test_sample_greedy_is_first_argmax():
     lg = _logits(64, 3072, 4.0, "f32", 5)
     lg[:, 1234] = lg.max(dim=1).values + 1.0
