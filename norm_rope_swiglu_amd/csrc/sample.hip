@@ -543,7 +543,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
         const uint32_t srt = wave_sort_desc(mkey);
         if (lane < m) sh.lead[wave * m + lane] = srt;
         if (tid == 0) sh.lead_bound = 0u;
-        lds_sync();   // the streamed batches stay in flight
+        lds_sync();   // the streamed batch stays in flight
         const int na = kWaves * m;
         uint32_t cand = 0u;
         if (tid < na) {
