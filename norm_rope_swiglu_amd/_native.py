@@ -75,8 +75,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m norm_rope_swiglu_amd.build` "
-                               "(or __graft_entry__.build()); there is no fallback path")
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m norm_rope_swiglu_amd.build`; "
+                               "there is no fallback path")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)

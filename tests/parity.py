@@ -102,6 +102,7 @@ def check_exact(name: str, y: torch.Tensor, ref: torch.Tensor) -> None:
 
 
 def dump(path: str) -> None:
-    os.makedirs(os.path.dirname(path), exist_ok=True)
+    if os.path.dirname(path):
+        os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(REPORT, f, indent=1)

@@ -21,7 +21,9 @@ import workloads as W
 from parity import check, check_exact, dump
 
 pytestmark = pytest.mark.gpu
-OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+# where the per-check parity report (every comparison's worst error and cosine) is written:
+# the file named by NRS_PARITY_REPORT, if set
+REPORT = os.environ.get("NRS_PARITY_REPORT")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,7 +32,8 @@ def gpu():
         pytest.skip("needs a GPU")
     nrs.lib()  # raises if the HIP library is missing: no fallback
     yield
-    dump(os.path.join(OUT, "parity_report.json"))
+    if REPORT:
+        dump(REPORT)
 
 
 def f32(v):
