@@ -472,6 +472,32 @@ def test_sample_long_rows_non_finite_logits_give_a_valid_index(dt):
     assert torch.all((tok >= 0) & (tok < V))
 
 
+@pytest.mark.parametrize("dt,vocab", [("bf16", 8192), ("bf16", 16384), ("bf16", 32000),
+                                      ("bf16", 65528), ("bf16", 65536), ("f32", 4096),
+                                      ("f32", 8200), ("f32", 32000), ("f32", 32768)])
+def test_sample_held_rows_token_only(dt, vocab):
+    # token-only rows of one to eight chunks per thread (the whole row held) with top_k <= 128
+    # are filtered against a bound from the threads' maxima: exactly one chunk per thread,
+    # partial last rounds, k = 1, 50 and 128, ties, all-equal rows (every entry passes the
+    # bound: the buffer overflows and the row is selected again), ramps, negative rows (the
+    # bound below zero: compared on order keys)
+    rows = 5
+    for k, seed in ((50, 81), (1, 82), (128, 83)):
+        lg = _logits(rows, vocab, 3.0, dt, seed)
+        sample_parity(lg, 0.9, k, _u(rows, seed + 10), f"sample/held/{dt}/V{vocab}/k{k}",
+                      want_probs=False)
+    t = _logits(rows, vocab, 2.0, dt, 84, ties=True)
+    sample_parity(t, 1.0, 64, _u(rows, 85), f"sample/held_ties/{dt}/V{vocab}", want_probs=False)
+    ramp = torch.linspace(-8.0, 8.0, vocab)
+    other = torch.stack([torch.zeros(vocab), ramp, ramp.flip(0), -(ramp.abs() + 1.0)])
+    stored = W.store(other, dt)
+    tok, _ = sample_parity(stored, 1.0, 40, torch.tensor([0.5, 0.0, 0.0, 0.3], dtype=torch.float32),
+                           f"sample/held_shapes/{dt}/V{vocab}", want_probs=False)
+    for r in (1, 2):   # u = 0: the first of the largest logits (bf16 rounding ties the ramp's ends)
+        row = stored[r].float()
+        assert tok[r] == int(torch.nonzero(row == row.max())[0])
+
+
 def test_sample_greedy_is_first_argmax():
     lg = _logits(64, 3072, 4.0, "f32", 5)
     lg[:, 1234] = lg.max(dim=1).values + 1.0
