@@ -69,6 +69,8 @@ constexpr int kRankMax = 256;
 // rows filtered against a bound take it from the waves' leading thread
 // maxima up to this top_k (a radix select over all the maxima beyond)
 constexpr int kLeadTopK = 128;
+// the template value of the kernel for rows longer than its held part
+constexpr int kLongRow = -9;
 
 // Order-preserving map of an fp32 value to uint32 (larger value, larger key);
 // -0 is folded onto +0 so equal values have equal keys.
@@ -397,9 +399,9 @@ struct SampleShared {
 
 // One row.  CPT > 0: thread t holds the row's chunks t, t + 1024, ... (at
 // most CPT of them) in registers; CPT == 0: every pass streams the row from
-// memory.  CPT < 0 (rows longer than -CPT chunks per thread, token only):
-// the row's first -CPT * 1024 chunks are held and selected as a row of their
-// own; their k-th largest key is a lower bound for the whole row's, so one
+// memory.  CPT < 0 (token only): the row's first chunks are held, the
+// whole row if CPT > kLongRow (-CPT chunks per thread), else 8 * 1024 of
+// them, and selected as a row of their own; their k-th largest key is a lower bound for the whole row's, so one
 // pass over the rest of the row appends every key at or above it to the kept
 // entries, and the sort of all of them gives the row's top k.  The row is read
 // once.  If the kept entries overflow the buffer (a row whose later logits
@@ -413,7 +415,11 @@ __device__ __attribute__((always_inline)) bool sample_row(
     using T = io_traits<IO>;
     constexpr int VEC = T::VEC;
     constexpr bool FILTER = CPT < 0;
-    constexpr int HC = FILTER ? -CPT : CPT;   // chunks held per thread
+    // CPT == kLongRow: a row longer than its held part (8 chunks per thread,
+    // every one in the row); other negative CPT: the whole row held, -CPT
+    // chunks per thread, the last round possibly partial
+    constexpr bool LONG = CPT == kLongRow;
+    constexpr int HC = LONG ? 8 : (FILTER ? -CPT : CPT);   // chunks held per thread
     constexpr int kDigitBits = HC > 0 ? 8 : 12;
     // (the select over the threads' maxima counts one key per thread)
     constexpr int kRep = FILTER ? 4 : (HC == 1 ? 8 : (HC > 0 ? 32 : 4));
@@ -459,7 +465,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
 #pragma unroll
         for (int j = 0; j < HC; ++j) {
             const int64_t c = tid + (int64_t)j * kThreads;   // (no branch: a chunk past the
-            held[j] = load16(x + (c < nchunks ? c : nchunks - 1) * VEC);   // row re-reads its last)
+            held[j] = load16(x + (LONG || c < nchunks ? c : nchunks - 1) * VEC);   // row re-reads its last)
         }
         load_batch(sa, nheld + tid);
     } else if constexpr (HC > 0) {
@@ -532,7 +538,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
     if constexpr (FILTER) {
         // the held chunks that lie in the row (at least one: such rows have at
         // least one chunk per thread)
-        const int64_t nv = (nchunks - tid + kThreads - 1) / kThreads;
+        const int64_t nv = LONG ? HC : (nchunks - tid + kThreads - 1) / kThreads;
         mkey = max_key_raw<IO, HC>(held, nv < HC ? (int)nv : HC);
     }
     uint32_t prefix = 0, pmask = 0;
@@ -732,7 +738,7 @@ __device__ __attribute__((always_inline)) bool sample_row(
 #pragma unroll
             for (int j = 0; j < HC; ++j) {
                 cs[j] = tid + (int64_t)j * kThreads;
-                masks[j] = (cs[j] < nchunks && bnd.any(held[j])) ? bnd.mask(held[j]) : 0u;
+                masks[j] = ((LONG || cs[j] < nchunks) && bnd.any(held[j])) ? bnd.mask(held[j]) : 0u;
             }
             append(masks, held, cs, HC);
         }
@@ -1001,7 +1007,7 @@ void launch_typed(int32_t *token, void *probs, const void *logits, int64_t rows,
     else if (per_thread <= 2) { if (bound) NRS_TS(-2); else NRS_TS(2); }
     else if (per_thread <= 4) { if (bound) NRS_TS(-4); else NRS_TS(4); }
     else if (per_thread <= 8) { if (bound) NRS_TS(-8); else NRS_TS(8); }
-    else NRS_TS(-8);
+    else NRS_TS(kLongRow);
 #undef NRS_TS
 }
 
