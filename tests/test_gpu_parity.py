@@ -382,6 +382,29 @@ def test_swiglu_extreme_gates(dt):
     check(f"swiglu_extremes/{dt}", out, oracle.swiglu(gu))
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_swiglu_gate_sweep_no_low_gate(dt):
+    # chunks whose gates are all >= -80 take the kernel's branch-free path
+    # (a hardware base-2 exponential on an exactly split exponent): a dense
+    # sweep of that range, its edge at -80 and just above, large and
+    # infinite gates (clamped there), and a NaN gate, each in chunks with no
+    # gate below -80
+    rng = np.random.default_rng(23)
+    n = 1 << 16
+    g = np.linspace(-80.0, 100.0, n)
+    edge = np.array([-80.0, np.nextafter(np.float32(-80.0), np.float32(0)), -79.5, 100.0,
+                     np.nextafter(np.float32(100.0), np.float32(200)), 150.0, 1e4, 3e38,
+                     np.inf, np.nan, 0.0, -0.0, 1e-30, -1e-30, 88.7, 89.0, 104.0, 127.0])
+    edge = np.repeat(edge, 8)            # whole chunks of one gate in either dtype
+    G = np.concatenate([g, edge])
+    U = rng.uniform(-1.0, 1.0, G.size)     # |g u| stays inside fp32's range
+    U[:n] = rng.standard_normal(n) * np.exp(rng.uniform(-20.0, 20.0, n))
+    U[:1024] = 1.0
+    gu = torch.from_numpy(np.concatenate([G, U])).to(torch.float32).to(dt).view(1, -1)
+    out = nrs.swiglu(cuda(gu))
+    check(f"swiglu_sweep/{dt}", out, oracle.swiglu(gu))
+
+
 def test_swiglu_strided_rows():
     big = _rand((40, 2 * 768 + 64), torch.bfloat16, 17, scale=4.0)
     gu = cuda(big)[:, 32 : 32 + 1536]
