@@ -407,7 +407,7 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
     T, H, I, nq, nkv, D, s = w.tokens, w.hidden, w.inter, w.n_q, w.n_kv, w.head_dim, 2
     res = {}
 
-    def rotated(name, fn, sets, byts, mix, row_bytes=0):
+    def rotated(name, fn, sets, byts, mix, row_bytes=0, row_pattern=None):
         t = time_graph(dev, fn, sets, K, R)
         gbs = byts / (t["us"] * 1e-6) / 1e9
         t.update(bytes=byts, GB_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
@@ -419,6 +419,8 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
             rc = ceiling(dev, *mix, ceil_cache, K, R, row_bytes=row_bytes)
             t.update(row_ceiling_us=rc["us"], row_ceiling_GB_s=rc["GB_s"],
                      frac_of_row_ceiling=round(rc["us"] / t["us"], 4))
+            if row_pattern:
+                t.update(row_ceiling_pattern=row_pattern)
         res[name] = t
         torch.cuda.empty_cache()
 
@@ -448,14 +450,17 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
             sets, byts, stream_mix("mrope_kv_append", T, H, I, nq, nkv, D, s))
     del sets
     # sampling over a text-sized vocabulary: 256 rows x 151936 bf16 logits (algorithmic
-    # bytes: the logits read once, u read and the token written); ceiling: read-only
+    # bytes: the logits read once, u read and the token written); ceilings: the flat
+    # read-only kernel over the logits, and the row-granular read of the sampler's own
+    # shape (one 1024-thread workgroup per row, reading it and nothing else)
     byts = 256 * 151936 * 2 + 256 * 8
     sets = [(torch.randn(256, 151936, device=dev).mul_(3.0).to(torch.bfloat16),
              torch.rand(256, device=dev), torch.empty(256, dtype=torch.int32, device=dev))
             for _ in range(rotation(byts))]
     rotated("softmax_topk_sample_256x151936_k50",
             lambda b: nrs.softmax_topk_sample(b[0], 1.0, 50, b[1], token=b[2]), sets, byts,
-            (1, 0, 256 * 151936 * 2))
+            (1, 0, 256 * 151936 * 2), row_bytes=151936 * 2,
+            row_pattern="read only: one 1024-thread workgroup per 303872-byte row")
     del sets
 
     # decode-size calls recorded in graphs over distinct inputs (so no host launch cost and

@@ -280,6 +280,12 @@ int nrs_null_graph_create(nrs_graph *out, int32_t n_nodes);
  *     workgroup, one chunk per thread; variant 1 = one wave per row, four
  *     rows per 256-thread workgroup.  It writes dst0 = src0 (XOR src1),
  *     dst1 = NOT of src0; bytes must be a whole number of rows.
+ *   row_bytes > 0 with n_read == 1 and n_write == 0: a row-granular read,
+ *     the access pattern of the sampler's long rows: one 1024-thread
+ *     workgroup per row of row_bytes (a multiple of 16, at most 1 GiB),
+ *     thread t reading chunks t, t + 1024, ..., its first 8 together, then
+ *     the rest 4 (variant 0) or 8 (variant 1) at a time; nothing is written;
+ *     bytes must be a whole number of rows, at most 2^31 - 1 of them.
  * The fastest variant at an op's read/write mix and size is the practical
  * ceiling the op is compared with.
  *   1 <= n_read + n_write; 0 <= variant <= 3 (0-1 with rows), other

@@ -17,7 +17,9 @@
 // Loads are nontemporal; calls that move under kStreamBytes in all use cached
 // accesses, as the ops do.  The ceiling of a read/write mix and size is the
 // fastest of the four.  With a row size, the copy is row-granular instead
-// (stream_rows_kernel): the ceiling of the norms' access pattern.
+// (stream_rows_kernel): the ceiling of the norms' access pattern; with a row
+// size and no writes it reads whole rows one workgroup each
+// (stream_rowread_kernel): the ceiling of the sampler's access pattern.
 //
 // This is a measurement aid, not an op of the pages: it gives the copy (1
 // read, 1 write), read-only, write-only, 2-read-1-write (SwiGLU's mix) and
@@ -107,6 +109,39 @@ __global__ __launch_bounds__(WAVE ? 256 : 64 * KIB) void stream_rows_kernel(
     }
 }
 
+// Row-granular reads: one 1024-thread workgroup per row of `cpr` 16-byte
+// chunks, thread t reading chunks t, t + 1024, ...: its first 8 issued
+// together, then the rest B at a time, every batch folded into a running XOR
+// that an empty asm statement consumes (nothing is written).  The access
+// pattern of the sampler's long rows, which are read once by one workgroup
+// each while the row's selection runs.
+template <int B, bool NT>
+__global__ __launch_bounds__(1024) void stream_rowread_kernel(const u32x4 *s0, int64_t cpr) {
+    constexpr int kHold = 8;
+    const u32x4 *p = s0 + (int64_t)blockIdx.x * cpr;
+    const int64_t t = threadIdx.x;
+    u32x4 acc = {0, 0, 0, 0};
+    u32x4 h[kHold];
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+        const int64_t c = t + 1024 * i;
+        h[i] = c < cpr ? load16_policy<NT>(p + c) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) acc ^= h[i];
+    for (int64_t c = t + 1024 * kHold; c < cpr; c += 1024 * B) {
+        u32x4 b[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int64_t cc = c + 1024 * i;
+            b[i] = cc < cpr ? load16_policy<NT>(p + cc) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) acc ^= b[i];
+    }
+    asm volatile("" ::"v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]));
+}
+
 template <int NR, int KIB, bool NT>
 void launch_rows_kib(void *d0, void *d1, const void *s0, const void *s1, int64_t rows, bool wave,
                      hipStream_t stream) {
@@ -163,6 +198,24 @@ hipError_t launch_stream_probe(void *d0, void *d1, const void *s0, const void *s
                                hipStream_t stream) {
     const int64_t n = bytes / 16;
     const bool nt = bytes * (n_read + n_write) >= kStreamBytes;
+    if (row_bytes > 0 && n_write == 0) {
+        // row-granular read: variant 0 streams the rest of a row 4 chunks per
+        // thread at a time (the sampler's batches), variant 1 8 at a time
+        const int64_t rows = bytes / row_bytes, cpr = row_bytes / 16;
+        const dim3 grid((unsigned)rows), block(1024);
+#define NRS_ROWREAD(B, NT)                                                                        \
+    hipLaunchKernelGGL((stream_rowread_kernel<B, NT>), grid, block, 0, stream,                    \
+                       (const u32x4 *)s0, cpr)
+        if (variant == 0) {
+            if (nt) NRS_ROWREAD(4, true);
+            else NRS_ROWREAD(4, false);
+        } else {
+            if (nt) NRS_ROWREAD(8, true);
+            else NRS_ROWREAD(8, false);
+        }
+#undef NRS_ROWREAD
+        return hipGetLastError();
+    }
     if (row_bytes > 0) {
         const int64_t rows = bytes / row_bytes;
         const int kib = (int)(row_bytes >> 10);

@@ -172,6 +172,9 @@ inline int check_topk_sample(const int32_t *token, const void *probs, const void
     return NRS_OK;
 }
 
+// Longest row of a row-granular read (one workgroup walks the row).
+constexpr int64_t kMaxReadRowBytes = (int64_t)1 << 30;
+
 inline bool row_size_ok(int64_t row_bytes) {
     const int64_t k = row_bytes >> 10;
     return row_bytes % 1024 == 0 &&
@@ -184,9 +187,17 @@ inline int check_stream_probe(const void *d0, const void *d1, const void *s0, co
     if (n_read < 0 || n_read > 2 || n_write < 0 || n_write > 2 || n_read + n_write == 0 ||
         variant < 0 || variant > 3)
         return NRS_ERR_ARG;
-    if (row_bytes != 0 && (n_read != n_write || n_read == 0 || variant > 1)) return NRS_ERR_ARG;
+    // rows: a row-granular copy (n_read == n_write) or a row-granular read
+    // (one source, no destination)
+    const bool row_read = row_bytes != 0 && n_read == 1 && n_write == 0;
+    if (row_bytes != 0 && ((n_read != n_write && !row_read) || n_read == 0 || variant > 1))
+        return NRS_ERR_ARG;
     if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > kMaxRows * 64) return NRS_ERR_SHAPE;
-    if (row_bytes < 0 || (row_bytes != 0 && (!row_size_ok(row_bytes) || bytes % row_bytes != 0)))
+    if (row_bytes < 0) return NRS_ERR_SHAPE;
+    if (row_read && (row_bytes % 16 != 0 || row_bytes > kMaxReadRowBytes ||
+                     bytes % row_bytes != 0 || bytes / row_bytes > kMaxRows))
+        return NRS_ERR_SHAPE;
+    if (row_bytes != 0 && !row_read && (!row_size_ok(row_bytes) || bytes % row_bytes != 0))
         return NRS_ERR_SHAPE;
     if (bytes == 0) return NRS_OK;
     const void *p[4] = {s0, s1, d0, d1};

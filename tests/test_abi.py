@@ -338,7 +338,16 @@ STREAM = [
     ((None, None, None, None, 1, 1, 0, 0, 0), OK),         # empty call: no launch
     ((P, None, P, None, 1, 1, 1024, 0, 4), ARG),       # no such variant
     ((P, None, P, None, 1, 1, 1024, 0, -1), ARG),
-    ((P, None, P, None, 1, 0, 4096, 1024, 0), ARG),   # rows move as many streams each way
+    ((P, P, P, None, 1, 2, 4096, 1024, 0), ARG),      # row copies move as many streams each way
+    ((P, None, P, P, 2, 0, 4096, 1024, 0), ARG),      # a row read takes one source
+    ((P, None, None, None, 0, 1, 4096, 1024, 0), ARG),    # rows: something is read
+    ((None, None, P, None, 1, 0, 4096, 1024, 2), ARG),    # row read: variants 0 and 1 only
+    ((None, None, P, None, 1, 0, 4096, 1000, 0), SHAPE),  # row read: whole 16-byte chunks
+    ((None, None, P, None, 1, 0, 4096, 1008, 0), SHAPE),  # row read: whole rows
+    ((None, None, P, None, 1, 0, 2**31, 2**30 + 16, 0), SHAPE),  # row read: rows up to 1 GiB
+    ((None, None, P, None, 1, 0, 2**31 * 32, 16, 0), SHAPE),     # row read: at most 2^31 - 1 rows
+    ((None, None, None, None, 1, 0, 1008, 1008, 0), NULL),       # row read needs its source
+    ((None, None, U, None, 1, 0, 1008, 1008, 0), ALIGN),
     ((P, None, P, None, 1, 1, 4096, 1024, 2), ARG),   # rows: variants 0 and 1 only
     ((P, None, P, None, 1, 1, 4096, 1000, 0), SHAPE), # rows of whole KiB
     ((P, None, P, None, 1, 1, 5120, 5120, 0), SHAPE), # 5 KiB rows are not built

@@ -70,6 +70,21 @@ def test_stream_probe_rows(kib, rows, n, variant):
         assert torch.equal(ddst[1].cpu(), ~src[0])
 
 
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("row_bytes,rows", [(16, 7), (1008, 3), (16384 * 16 + 48, 2),
+                                            (151936 * 2, 5), (8 * 1024 * 16, 3)])
+def test_stream_probe_row_read(row_bytes, rows, variant):
+    # the row-granular read (the sampler's shape) completes, leaves its source
+    # untouched and writes nothing: rows shorter than, equal to and longer than
+    # the 8 chunks per thread it issues first, with a partial last batch
+    nbytes = rows * row_bytes
+    src = _words(nbytes, 31)
+    d = src.cuda()
+    nrs.stream_probe(1, 0, [d], [], nbytes, variant, row_bytes=row_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(d.cpu(), src)
+
+
 def test_stream_probe_empty_call():
     nrs.stream_probe(1, 1, [torch.empty(16, dtype=torch.uint8, device="cuda")],
                      [torch.empty(16, dtype=torch.uint8, device="cuda")], 0)
