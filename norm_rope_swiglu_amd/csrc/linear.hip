@@ -187,19 +187,26 @@ __global__ __launch_bounds__(64 * S) void rmsnorm_linear_kernel(
 // than 64 * CPL chunks (CPL = 8: more than 4096 inputs) take NP passes, the
 // next pass's weight loads issued before this pass's products.
 constexpr int kGemvRowsPerWave = 2;
-constexpr int kGemvWaves = 4;           // waves per block
+constexpr int kGemvWaves = 4;           // waves per block (kGemvWavesWide for wide outputs)
+// Every block stages all x rows in LDS, so the grid re-reads x from L2 once
+// per block.  Wide outputs take blocks of 8 waves, half the blocks: measured
+// on MI355X (graph of 28 calls with distinct weights) 5 x 2048 -> 12288
+// 12.25 -> 11.9 us, while 5 x 2048 -> 4096 (one block per CU with 8 waves)
+// went 6.2 -> 6.3 us and keeps 4.
+constexpr int kGemvWavesWide = 8;
+constexpr int64_t kGemvWideOut = 8192;   // outputs from which blocks are wide
 constexpr int kGemvMaxXChunks = 2048;   // rows x chunks of x staged in LDS: 32 KiB
 constexpr int kGemvMaxPasses = 4;       // 64 lanes x 8 chunks x 4 passes = kGemvMaxXChunks
 
-template <int M, int CPL, int NP>
-__global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
+template <int M, int CPL, int NP, int W>
+__global__ __launch_bounds__(64 * W) void rmsnorm_gemv_kernel(
     __bf16 *out, const __bf16 *x, const __bf16 *w, int32_t nchunks, int64_t n_out,
     int64_t x_stride, int64_t w_stride, int64_t out_stride, fastdiv div_nchunks, float inv_n,
     float eps) {
     constexpr int RPW = kGemvRowsPerWave;
-    constexpr int NTH = 64 * kGemvWaves;
+    constexpr int NTH = 64 * W;
     // x chunks each thread stages: M * nchunks <= M * 64 * CPL * NP <= NTH * XPT
-    constexpr int XPT = (M * CPL * NP + kGemvWaves - 1) / kGemvWaves;
+    constexpr int XPT = (M * CPL * NP + W - 1) / W;
     static_assert(NP == 1 || CPL == 8, "only 8-chunk lanes take several passes");
     static_assert(NP <= kGemvMaxPasses, "a row fits kGemvMaxXChunks");
     extern __shared__ u32x4 xs[];            // [M][nchunks]
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
         const int m = (int)div((uint32_t)e, div_nchunks), c = e - m * nchunks;
         xv[k] = load16(x + (int64_t)m * x_stride + c * 8);
     }
-    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * RPW;   // the wave's first weight row
+    const int64_t row0 = ((int64_t)blockIdx.x * W + wave) * RPW;   // the wave's first weight row
     u32x4 wv[NP > 1 ? 2 : 1][RPW][CPL];   // this pass's chunks and the next pass's loads
     auto load_w = [&](int p, int buf) {
 #pragma unroll
@@ -237,9 +244,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void rmsnorm_gemv_kernel(
     for (int k = 0; k < XPT; ++k) xs[min((int)threadIdx.x + NTH * k, nx - 1)] = xv[k];
     __syncthreads();
 
-    // 2. each row's 1 / rms from the staged copy (wave w takes rows w, w + kGemvWaves, ...)
+    // 2. each row's 1 / rms from the staged copy (wave w takes rows w, w + W, ...)
 #pragma unroll
-    for (int m = wave; m < M; m += kGemvWaves) {
+    for (int m = wave; m < M; m += W) {
         float sq = 0.0f;
         for (int c = lane; c < nchunks; c += 64) {
             const u32x4 v = xs[m * nchunks + c];
@@ -614,24 +621,28 @@ hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, in
     const int32_t nchunks = (int32_t)(n_in / 8);
     const int cpl = nchunks <= 64 ? 1 : nchunks <= 128 ? 2 : nchunks <= 256 ? 4 : 8;
     const int np = (nchunks + 64 * cpl - 1) / (64 * cpl);
-    const int64_t per_block = kGemvWaves * kGemvRowsPerWave;
-    const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(64 * kGemvWaves);
+    // wide blocks where measured faster: 4 chunks per lane (1032-2048 inputs)
+    const bool wide = cpl == 4 && np == 1 && n_out >= kGemvWideOut;
+    const int waves = wide ? kGemvWavesWide : kGemvWaves;
+    const int64_t per_block = waves * kGemvRowsPerWave;
+    const dim3 grid((unsigned)((n_out + per_block - 1) / per_block)), block(64 * waves);
     const size_t lds = (size_t)rows * nchunks * sizeof(u32x4);
     const fastdiv dn = make_fastdiv((uint32_t)nchunks);
-#define NRS_GEMV(M, C, P)                                                                        \
-    hipLaunchKernelGGL((rmsnorm_gemv_kernel<M, C, P>), grid, block, lds, stream, (__bf16 *)out,  \
-                       (const __bf16 *)x, (const __bf16 *)w, nchunks, n_out, xs, ws, os, dn,     \
-                       inv_n, eps)
-#define NRS_GEMV_M(C)                                                                            \
+#define NRS_GEMV_W(M, C, P, W)                                                                   \
+    hipLaunchKernelGGL((rmsnorm_gemv_kernel<M, C, P, W>), grid, block, lds, stream,              \
+                       (__bf16 *)out, (const __bf16 *)x, (const __bf16 *)w, nchunks, n_out, xs,  \
+                       ws, os, dn, inv_n, eps)
+#define NRS_GEMV(M, C, P) NRS_GEMV_W(M, C, P, kGemvWaves)
+#define NRS_GEMV_M(C, W)                                                                         \
     switch (rows) {                                                                              \
-        case 1: NRS_GEMV(1, C, 1); break;                                                        \
-        case 2: NRS_GEMV(2, C, 1); break;                                                        \
-        case 3: NRS_GEMV(3, C, 1); break;                                                        \
-        case 4: NRS_GEMV(4, C, 1); break;                                                        \
-        case 5: NRS_GEMV(5, C, 1); break;                                                        \
-        case 6: NRS_GEMV(6, C, 1); break;                                                        \
-        case 7: NRS_GEMV(7, C, 1); break;                                                        \
-        default: NRS_GEMV(8, C, 1); break;                                                       \
+        case 1: NRS_GEMV_W(1, C, 1, W); break;                                                   \
+        case 2: NRS_GEMV_W(2, C, 1, W); break;                                                   \
+        case 3: NRS_GEMV_W(3, C, 1, W); break;                                                   \
+        case 4: NRS_GEMV_W(4, C, 1, W); break;                                                   \
+        case 5: NRS_GEMV_W(5, C, 1, W); break;                                                   \
+        case 6: NRS_GEMV_W(6, C, 1, W); break;                                                   \
+        case 7: NRS_GEMV_W(7, C, 1, W); break;                                                   \
+        default: NRS_GEMV_W(8, C, 1, W); break;                                                  \
     }
     if (np > 1) {
         // rows * nchunks <= kGemvMaxXChunks: 2 passes (513-1024 chunks) take
@@ -645,12 +656,14 @@ hipError_t launch_gemv(void *out, const void *x, const void *w, int64_t rows, in
         } else {
             NRS_GEMV(3, 8, 2);
         }
-    } else if (cpl == 1) NRS_GEMV_M(1)
-    else if (cpl == 2) NRS_GEMV_M(2)
-    else if (cpl == 4) NRS_GEMV_M(4)
-    else NRS_GEMV_M(8)
+    } else if (cpl == 1) NRS_GEMV_M(1, kGemvWaves)
+    else if (cpl == 2) NRS_GEMV_M(2, kGemvWaves)
+    else if (cpl == 4 && wide) NRS_GEMV_M(4, kGemvWavesWide)
+    else if (cpl == 4) NRS_GEMV_M(4, kGemvWaves)
+    else NRS_GEMV_M(8, kGemvWaves)
 #undef NRS_GEMV_M
 #undef NRS_GEMV
+#undef NRS_GEMV_W
     return hipGetLastError();
 }
 

@@ -95,13 +95,15 @@ def test_output_widths(n_out):
                                              (8, 2048, 7), (2, 520, 4099),
                                              (1, 8192, 33), (2, 6144, 70), (1, 16384, 9),
                                              (3, 5456, 17), (1, 12296, 5), (2, 4104, 12),
-                                             (1, 4104, 3)])
+                                             (1, 4104, 3), (1, 2048, 8200), (8, 1600, 8197),
+                                             (3, 1032, 8195), (5, 2048, 8192)])
 def test_gemv_shapes(rows, n_in, n_out):
     # bf16 decode rows (<= 8, x within 2048 chunks): one wave per pair of weight rows,
     # 1, 2, 4 or 8 chunks per lane with part-filled last chunk groups, blocks of 8 weight
     # rows with part-filled last blocks, and the largest x staged in LDS; rows of more
     # than 512 chunks (over 4096 inputs) in 2, 3 or 4 passes of 8 chunks per lane, with
-    # part-filled last passes
+    # part-filled last passes; outputs from 8192 on at 1032-2048 inputs take 8-wave blocks
+    # (16 weight rows a block), with part-filled last blocks
     x, w = lin_inputs(rows, n_in, n_out, "bf16", 11)
     lin_parity(x, w, 1e-6, f"lin/gemv/{rows}x{n_in}x{n_out}")
 
