@@ -81,10 +81,10 @@ __device__ inline void rotate_chunks(const f32x2 *tab, const u32x4 &lo, const u3
 
 template <typename IO, bool NT>
 __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
-    IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int64_t tokens, int32_t n_q,
-    int32_t head_dim, int64_t q_stride, int64_t k_stride, int32_t sec_t, int32_t sec_th,
-    int32_t tpb, int32_t per_tok, int32_t cph, fastdiv div_half, fastdiv div_q_ipt,
-    fastdiv div_k_ipt, fastdiv div_cph, mrope_freqs fr) {
+    [[maybe_unused]] mrope_freqs fr, IO *q, IO *k, const int32_t *pos, int64_t pos_stride,
+    int64_t tokens, int32_t n_q, int32_t head_dim, int64_t q_stride, int64_t k_stride,
+    int32_t sec_t, int32_t sec_th, int32_t tpb, int32_t per_tok, int32_t cph, fastdiv div_half,
+    fastdiv div_q_ipt, fastdiv div_k_ipt, fastdiv div_cph) {
     constexpr int VEC = io_traits<IO>::VEC;
     extern __shared__ f32x2 table[];  // [tpb][half] = (cos, sin)
     const int half = head_dim >> 1;
@@ -98,11 +98,16 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     // first (token-major, so consecutive tokens' q rows are walked in one
     // run), then its k items
     const int q_items = ntok * n_q * cph;
+    // the fastdiv fields by value: selecting between the two structs made the
+    // compiler load the chosen one from the kernel arguments per lane, and
+    // wait for it, before the data loads below
+    const uint32_t qm = div_q_ipt.m, qs = div_q_ipt.s, km = div_k_ipt.m, ks = div_k_ipt.s;
     auto locate = [&](int i, int &tab) -> IO * {
         const bool is_q = i < q_items;
         const int j = is_q ? i : i - q_items;
         const int hpt = is_q ? n_q : per_tok / cph - n_q;   // heads per token
-        const int tl = (int)div((uint32_t)j, is_q ? div_q_ipt : div_k_ipt);
+        const uint32_t m = is_q ? qm : km, sh = is_q ? qs : ks;
+        const int tl = (int)((__umulhi((uint32_t)j, m) + (uint32_t)j) >> sh);
         const int rem = j - tl * hpt * cph;
         const int head = (int)div((uint32_t)rem, div_cph);
         const int c = rem - head * cph;
@@ -118,22 +123,63 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
         store16_policy<NT>(p + half, rhi);
     };
 
-    // 1. this thread's first item: issue its loads before anything else
-    IO *p0 = nullptr;
-    int tab0 = 0;
-    u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
-    if (tid < items) {
-        p0 = locate(tid, tab0);
-        lo0 = load16_policy<NT>(p0);
-        hi0 = load16_policy<NT>(p0 + half);
-    }
+    // 0. the position and frequency of this thread's first two (cos, sin)
+    //    entries, loaded before its data: loads complete in order, so loaded
+    //    after the data they would make the table, and the block barrier
+    //    behind it, wait for this thread's data as well.  The frequencies (fr,
+    //    the first kernel argument: offset 0 of the kernel argument segment)
+    //    are read through an opaque global pointer, as in mrope_wave_kernel.
+    typedef const __attribute__((address_space(1))) double gdouble;
+    const void *ka = (const void *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    gdouble *const wg = (gdouble *)ka;
+    const int n_ang = ntok * half;
+    auto entry = [&](int e, int32_t &p_out, double &w_out) {
+        const int tl = (int)div((uint32_t)e, div_half);
+        const int j = e - tl * half;
+        const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
+        p_out = pos[s * pos_stride + tok0 + tl];
+        w_out = wg[j];
+    };
+    int32_t pe0, pe1;
+    double we0, we1;
+    entry(tid < n_ang ? tid : 0, pe0, we0);   // (no branch: entry 0 always exists)
+    entry(tid + nthreads < n_ang ? tid + nthreads : 0, pe1, we1);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the block's angle table
-    build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half, fr);
+    // 1. this thread's first item: its data loads, with no branch (a thread
+    //    past the block's items re-reads its last item and stores nothing),
+    //    so the table below waits for the position loads alone
+    const bool has0 = tid < items;
+    int tab0 = 0;
+    IO *const p0 = locate(has0 ? tid : items - 1, tab0);
+    const u32x4 lo0 = load16_policy<NT>(p0);
+    const u32x4 hi0 = load16_policy<NT>(p0 + half);
+    __builtin_amdgcn_sched_barrier(0);
+    // (the positions are used from here on only, or the compiler converts
+    // them before issuing the data loads, waiting for them there)
+    asm volatile("" : "+v"(pe0), "+v"(pe1), "+v"(we0), "+v"(we1));
+
+    // 2. the block's angle table, with the arithmetic of build_angle_table;
+    //    the first two entries of a thread outside any loop (a loop that may
+    //    load made the compiler wait for every load, the data too, on entry)
+    auto angle = [](int32_t pv, double wv) {
+        const double turns = ((double)pv * wv) * kInvTwoPi;
+        const float t = (float)(turns - __builtin_rint(turns));
+        return f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
+    };
+    if (tid < n_ang) table[tid] = angle(pe0, we0);
+    if (tid + nthreads < n_ang) table[tid + nthreads] = angle(pe1, we1);
+    for (int e = tid + 2 * nthreads; e < n_ang; e += nthreads) {
+        int32_t pv;
+        double wv;
+        entry(e, pv, wv);
+        table[e] = angle(pv, wv);
+    }
     __syncthreads();
 
     // 3. rotate; blocks with more items than threads loop over the rest
-    if (p0) rotate_store(p0, tab0, lo0, hi0);
+    if (has0) rotate_store(p0, tab0, lo0, hi0);
     for (int i = tid + nthreads; i < items; i += nthreads) {
         int tab;
         IO *p = locate(i, tab);
@@ -662,9 +708,9 @@ hipError_t launch_mrope(void *q, void *k, const int32_t *pos, int64_t pos_stride
                   dk = make_fastdiv((uint32_t)(k_ipt > 0 ? k_ipt : 1)), dc = make_fastdiv((uint32_t)cph);
     const dim3 grid((unsigned)blocks), block(threads);
 #define NRS_MROPE(IO, NT)                                                                        \
-    hipLaunchKernelGGL((mrope_kernel<IO, NT>), grid, block, lds, stream, (IO *)q, (IO *)k, pos,  \
-                       pos_stride, tokens, n_q, head_dim, q_stride, k_stride, sec_t,             \
-                       sec_t + sec_h, tpb, per_tok, cph, dh, dq, dk, dc, fr)
+    hipLaunchKernelGGL((mrope_kernel<IO, NT>), grid, block, lds, stream, fr, (IO *)q, (IO *)k,   \
+                       pos, pos_stride, tokens, n_q, head_dim, q_stride, k_stride, sec_t,        \
+                       sec_t + sec_h, tpb, per_tok, cph, dh, dq, dk, dc)
     if (dtype == 0) {
         if (nt) NRS_MROPE(float, true);
         else NRS_MROPE(float, false);
