@@ -39,11 +39,19 @@ constexpr int kMaxThreads = 1024;
 template <bool NT> constexpr int narrow_per_thread() { return NT ? 2 : 1; }
 }  // namespace
 
-// (cos, sin) of every (token, pair) of the block's tokens into LDS: the angle
-// p * w_j in fp64 (w_j from the host in fp64), converted to turns, the nearest
-// whole turn removed in fp64 (exact), and the fraction, |t| <= 1/2, rounded to
-// fp32 for the hardware v_sin_f32 / v_cos_f32, which take turns: measured max
-// abs error 1.3e-7 over [-1/2, 1/2) on MI355X.
+// (cos, sin) of the angle p * w (w = w_j from the host in fp64): the product
+// formed in fp64, converted to turns, the nearest whole turn removed in fp64
+// (exact), and the fraction, |t| <= 1/2, rounded to fp32 for the hardware
+// v_sin_f32 / v_cos_f32, which take turns: measured max abs error 1.3e-7 over
+// [-1/2, 1/2) on MI355X.  Every kernel here forms its angles with this, so
+// they all give the same bits.
+__device__ inline f32x2 angle_cs(int32_t p, double w) {
+    const double turns = ((double)p * w) * kInvTwoPi;
+    const float t = (float)(turns - __builtin_rint(turns));
+    return f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
+}
+
+// (cos, sin) of every (token, pair) of the block's tokens into LDS.
 __device__ inline void build_angle_table(f32x2 *table, const int32_t *pos, int64_t pos_stride,
                                          int64_t tok0, int ntok, int half, int32_t sec_t,
                                          int32_t sec_th, const fastdiv &div_half,
@@ -53,10 +61,51 @@ __device__ inline void build_angle_table(f32x2 *table, const int32_t *pos, int64
         const int tl = (int)div((uint32_t)e, div_half);
         const int j = e - tl * half;
         const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
-        const double p = (double)pos[s * pos_stride + tok0 + tl];
-        const double turns = (p * fr.w[j]) * kInvTwoPi;
-        const float t = (float)(turns - __builtin_rint(turns));
-        table[e] = f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
+        table[e] = angle_cs(pos[s * pos_stride + tok0 + tl], fr.w[j]);
+    }
+}
+
+// The frequencies w_j of a kernel whose first argument is its mrope_freqs,
+// through an opaque global pointer to the kernel-argument segment: read as
+// the struct, the compiler treats them as invariant and may move their loads
+// behind the data loads (and taking the struct's address copies it to
+// scratch).
+typedef const __attribute__((address_space(1))) double gdouble;
+__device__ inline gdouble *kernarg_freqs() {
+    const void *ka = (const void *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    return (gdouble *)ka;
+}
+
+// Position and frequency of (cos, sin) entry e of the block's tokens (token
+// tok0 + e / half, pair e % half).
+__device__ inline void angle_input(int e, const int32_t *pos, int64_t pos_stride, int64_t tok0,
+                                   int half, int32_t sec_t, int32_t sec_th,
+                                   const fastdiv &div_half, gdouble *wg, int32_t &p, double &w) {
+    const int tl = (int)div((uint32_t)e, div_half);
+    const int j = e - tl * half;
+    const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
+    p = pos[s * pos_stride + tok0 + tl];
+    w = wg[j];
+}
+
+// The block's table when each thread loaded the inputs of its first two
+// entries (tid and tid + blockDim) ahead of its data: those two are formed
+// outside any loop (a loop that may load made the compiler wait for every
+// load, the data too, on entry), further entries load their own.
+__device__ inline void build_angle_table_from(f32x2 *table, int n_ang, int32_t p0, double w0,
+                                              int32_t p1, double w1, const int32_t *pos,
+                                              int64_t pos_stride, int64_t tok0, int half,
+                                              int32_t sec_t, int32_t sec_th,
+                                              const fastdiv &div_half, gdouble *wg) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    if (tid < n_ang) table[tid] = angle_cs(p0, w0);
+    if (tid + nth < n_ang) table[tid + nth] = angle_cs(p1, w1);
+    for (int e = tid + 2 * nth; e < n_ang; e += nth) {
+        int32_t p;
+        double w;
+        angle_input(e, pos, pos_stride, tok0, half, sec_t, sec_th, div_half, wg, p, w);
+        table[e] = angle_cs(p, w);
     }
 }
 
@@ -126,25 +175,15 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     // 0. the position and frequency of this thread's first two (cos, sin)
     //    entries, loaded before its data: loads complete in order, so loaded
     //    after the data they would make the table, and the block barrier
-    //    behind it, wait for this thread's data as well.  The frequencies (fr,
-    //    the first kernel argument: offset 0 of the kernel argument segment)
-    //    are read through an opaque global pointer, as in mrope_wave_kernel.
-    typedef const __attribute__((address_space(1))) double gdouble;
-    const void *ka = (const void *)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ka));
-    gdouble *const wg = (gdouble *)ka;
+    //    behind it, wait for this thread's data as well
+    gdouble *const wg = kernarg_freqs();
     const int n_ang = ntok * half;
-    auto entry = [&](int e, int32_t &p_out, double &w_out) {
-        const int tl = (int)div((uint32_t)e, div_half);
-        const int j = e - tl * half;
-        const int s = j < sec_t ? 0 : (j < sec_th ? 1 : 2);
-        p_out = pos[s * pos_stride + tok0 + tl];
-        w_out = wg[j];
-    };
     int32_t pe0, pe1;
     double we0, we1;
-    entry(tid < n_ang ? tid : 0, pe0, we0);   // (no branch: entry 0 always exists)
-    entry(tid + nthreads < n_ang ? tid + nthreads : 0, pe1, we1);
+    angle_input(tid < n_ang ? tid : 0, pos, pos_stride, tok0, half, sec_t, sec_th, div_half, wg,
+                pe0, we0);   // (no branch: entry 0 always exists)
+    angle_input(tid + nthreads < n_ang ? tid + nthreads : 0, pos, pos_stride, tok0, half, sec_t,
+                sec_th, div_half, wg, pe1, we1);
     __builtin_amdgcn_sched_barrier(0);
 
     // 1. this thread's first item: its data loads, with no branch (a thread
@@ -160,22 +199,9 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
     // them before issuing the data loads, waiting for them there)
     asm volatile("" : "+v"(pe0), "+v"(pe1), "+v"(we0), "+v"(we1));
 
-    // 2. the block's angle table, with the arithmetic of build_angle_table;
-    //    the first two entries of a thread outside any loop (a loop that may
-    //    load made the compiler wait for every load, the data too, on entry)
-    auto angle = [](int32_t pv, double wv) {
-        const double turns = ((double)pv * wv) * kInvTwoPi;
-        const float t = (float)(turns - __builtin_rint(turns));
-        return f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
-    };
-    if (tid < n_ang) table[tid] = angle(pe0, we0);
-    if (tid + nthreads < n_ang) table[tid + nthreads] = angle(pe1, we1);
-    for (int e = tid + 2 * nthreads; e < n_ang; e += nthreads) {
-        int32_t pv;
-        double wv;
-        entry(e, pv, wv);
-        table[e] = angle(pv, wv);
-    }
+    // 2. the block's angle table
+    build_angle_table_from(table, n_ang, pe0, we0, pe1, we1, pos, pos_stride, tok0, half, sec_t,
+                           sec_th, div_half, wg);
     __syncthreads();
 
     // 3. rotate; blocks with more items than threads loop over the rest
@@ -199,11 +225,10 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kernel(
 // CPH lanes away in the same wave and arrives by a lane swizzle (chunk
 // groups of a head are 2 * CPH lanes, aligned, since a wave starts at a
 // multiple of 64 chunks and a token holds whole heads), and the wave builds
-// the (cos, sin) entries of its own tokens in its own LDS slice, with the
-// arithmetic of build_angle_table (so the results are those of the kernels
-// above, bit for bit).  A wave's chunks never mix q and k: k's waves start
-// on a fresh wave.  Chunk indices are 32-bit: the launcher splits the tokens
-// into slabs.
+// the (cos, sin) entries of its own tokens in its own LDS slice with
+// angle_cs (so the results are those of the kernels above, bit for bit).  A
+// wave's chunks never mix q and k: k's waves start on a fresh wave.  Chunk
+// indices are 32-bit: the launcher splits the tokens into slabs.
 template <typename IO, bool NT, int CPH>
 __global__ __launch_bounds__(64) void mrope_wave_kernel(
     [[maybe_unused]] mrope_freqs fr, IO *q, IO *k, const int32_t *pos, int64_t pos_stride, int32_t tokens,
@@ -231,14 +256,9 @@ __global__ __launch_bounds__(64) void mrope_wave_kernel(
     const int32_t t_first = (int32_t)div((uint32_t)c0, dv);
     const int32_t t_last = (int32_t)div((uint32_t)min(c0 + 63, n - 1), dv);
     const int n_ang = (t_last - t_first + 1) * half;   // entries of the wave's tokens
-    // the frequencies (fr, the first kernel argument: offset 0 of the kernel
-    // argument segment) through an opaque global pointer: read as fr.w[j],
-    // the compiler treats them as invariant and sank the first load behind
-    // the data load below; taking fr's address copied it to scratch
-    typedef const __attribute__((address_space(1))) double gdouble;
-    const void *ka = (const void *)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ka));
-    gdouble *const wg = (gdouble *)ka;
+    // the frequencies through the kernel-argument pointer (kernarg_freqs):
+    // read as fr.w[j], the compiler sank the first load behind the data load
+    gdouble *const wg = kernarg_freqs();
     auto entry = [&](int e, int32_t &p_out, double &w_out) {
         const int tt = (int)div((uint32_t)e, div_half);
         const int j = e - tt * half;
@@ -269,9 +289,7 @@ __global__ __launch_bounds__(64) void mrope_wave_kernel(
         int32_t pe = p0;
         double we = w0;
         if (e != lane) entry(e, pe, we);
-        const double turns = ((double)pe * we) * kInvTwoPi;
-        const float t = (float)(turns - __builtin_rint(turns));
-        table[e] = f32x2{__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t)};
+        table[e] = angle_cs(pe, we);
     }
     __syncthreads();   // one wave: orders its own LDS writes before the reads
 
@@ -375,7 +393,9 @@ __global__ __launch_bounds__(kMaxThreads) void mrope_kv_kernel(
     }
     const int64_t b0 = seq_idx[t0], sl0 = slot[t0];   // t0 = tok0 for idle threads: no branch
 
-    // 2. the block's angle table
+    // 2. the block's angle table (here the position loads follow the data:
+    //    loading them first, as mrope_kernel does, measured no faster at
+    //    32768 tokens x 16 q / 8 kv heads of 128)
     build_angle_table(table, pos, pos_stride, tok0, ntok, half, sec_t, sec_th, div_half, fr);
     __syncthreads();
 
