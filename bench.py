@@ -449,6 +449,19 @@ def measure_next(dev, w, ceil_cache, K=20, R=11):
                                                              w.theta, b[3], b[4], seq0, slots),
             sets, byts, stream_mix("mrope_kv_append", T, H, I, nq, nkv, D, s))
     del sets
+    # the same append for a 2048-token prefill (the first 2048 tokens, a 2048-slot cache)
+    Tp = 2048
+    byts = algorithmic_bytes("mrope_kv_append", Tp, H, I, nq, nkv, D, s)
+    sets = []
+    for _ in range(rotation(byts)):
+        kc = torch.empty(1, nkv, Tp, D, dtype=L.k.dtype, device=dev)
+        sets.append((L.q[:Tp].clone(), L.k[:Tp].clone(), torch.empty_like(L.k[:Tp]).normal_(), kc,
+                     torch.empty_like(kc)))
+    rotated("mrope_kv_append_prefill2048",
+            lambda b: nrs.mrope_kv_append(b[0], b[1], b[2], w.pos, w.sections, w.theta, b[3], b[4],
+                                          seq0[:Tp], slots[:Tp]),
+            sets, byts, stream_mix("mrope_kv_append", Tp, H, I, nq, nkv, D, s))
+    del sets
     # sampling over a text-sized vocabulary: 256 rows x 151936 bf16 logits (algorithmic
     # bytes: the logits read once, u read and the token written); ceilings: the flat
     # read-only kernel over the logits, and the row-granular read of the sampler's own
